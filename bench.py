@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Throughput of rolling-window decode attention with exact RoPE re-basing.
+
+One step = for each of the 36 layers: a8r_append_kv (one new token per stream,
+all 64 streams in one call) then a8r_decode_attn (all 64 streams in one call),
+on the 3B-class GQA shape (16 query / 2 KV heads, head_dim 128, bf16 ring,
+W = 4096).  Streams start at seeded absolute positions in [0, 1e6) and ring
+offsets in [0, 4096) and are pre-filled to a full window before timing; inputs
+for the timed steps are pre-staged in HBM (a pool of distinct steps cycled
+through).  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 1000] [--warmup 20] [--workload qwen3b_batch64]
+
+``--workload qwen3b_chunk8`` measures the 8-position chunk path instead.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn steps/sec + KV HBM GB/s (% roofline), 3B-class GQA, W=4096, batch 64"
+HBM_PEAK_GBPS = 8000.0
+BF16_DENSE_TFLOPS = 2500.0
+POOL = 16
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "rolling_kv_cache_ring_amd", "csrc", "a8r_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3b_batch64", choices=["qwen3b_batch64", "qwen3b_chunk8"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl, live):
+    """Bytes one attention launch (one layer, all streams) must move: the live
+    K and V windows, the queries and the outputs."""
+    e = 2
+    kv = wl.n_streams * wl.n_kv_heads * live * wl.head_dim * e * 2
+    q = wl.n_streams * wl.chunk * wl.n_q_heads * wl.head_dim * e
+    return kv + 2 * q
+
+
+def append_bytes(wl):
+    return wl.n_streams * wl.chunk * wl.n_kv_heads * wl.head_dim * 2 * 2 * 2   # read + write K and V
+
+
+def attention_flops(wl, live):
+    # 4 * D * Hq * sum over queries of keys seen (QK^T and PV, 2 flops per MAC)
+    c = wl.chunk
+    keys = sum(live - c + 1 + j for j in range(c))
+    return 4 * wl.head_dim * wl.n_q_heads * keys * wl.n_streams
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
+    on the current kernel source; else None."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+        r = rec.get(workload)
+        if r and r.get("kernel_sha256_16") == kernel_hash():
+            return r.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(wl, seconds):
+    """Time the float64 oracle on host cores on a bounded sample of the same
+    workload: full-window decode (or chunk) attention for as many (layer, stream)
+    pairs as fit in ``seconds``, scaled to steps/s."""
+    import threadpoolctl
+    import synth
+    from oracle.attention import chunk_rebased
+    w, hkv, hq, d, c = wl.window, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.chunk
+    rng = np.random.default_rng(0)
+    k = synth.round_bf16(rng.standard_normal((w, hkv, d)).astype(np.float32)).astype(np.float64)
+    v = synth.round_bf16(rng.standard_normal((w, hkv, d)).astype(np.float32)).astype(np.float64)
+    q = synth.round_bf16(rng.standard_normal((c, hq, d)).astype(np.float32)).astype(np.float64)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    chunk_rebased(q, k, v)               # warm-up
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        chunk_rebased(q, k, v)
+        n += 1
+    dt = time.perf_counter() - t0
+    pairs_per_step = wl.n_layers * wl.n_streams
+    return {
+        "value": round(n / dt / pairs_per_step, 6),
+        "unit": "steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{n} (layer, stream) attention calls of the float64 numpy oracle over a full "
+                   f"W={w} window ({hq}/{hkv} heads, D={d}, {c} quer{'y' if c == 1 else 'ies'}) in "
+                   f"{dt:.1f} s; one step = {pairs_per_step} such calls; BLAS threads={threads}, "
+                   f"host cpus={len(os.sched_getaffinity(0))}"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(streams shard across GPUs with no exchange; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import rolling_kv_cache_ring_amd as a8r
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    a8r.lib()  # fails loudly if the HIP library is missing
+
+    wl = synth.WORKLOADS[args.workload]
+    B, NL, hq, hkv, d, w, c = (wl.n_streams, wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                               wl.window, wl.chunk)
+    stream = torch.cuda.current_stream()
+    cfg = a8r.make_config(NL, B, hq, hkv, d, w, w, True)
+    cache = a8r.Cache(cfg, stream=stream.cuda_stream)
+
+    # seeded start states; pre-fill each stream to min(P0, W) tokens ending at P0 - 1
+    p0, r0 = synth.start_states(wl)
+    n_pre = np.minimum(p0, w)
+    cache.reset(0, p0 - n_pre, (r0 - n_pre) % w)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0xA8)
+    bf = torch.bfloat16
+    fill = torch.randn((B, w, hkv, d), device="cuda", generator=gen).to(bf).view(torch.int16)
+    fill_v = torch.randn((B, w, hkv, d), device="cuda", generator=gen).to(bf).view(torch.int16)
+    for layer in range(NL):
+        for b in range(B):
+            n = int(n_pre[b])
+            if n:
+                cache.append_kv(layer, b, 1, n, fill[b:b + 1, :n], fill_v[b:b + 1, :n],
+                                want_bookkeeping=False)
+    del fill, fill_v
+    torch.cuda.synchronize()
+
+    kpool = torch.randn((POOL, NL, B, c, hkv, d), device="cuda", generator=gen).to(bf).view(torch.int16)
+    vpool = torch.randn((POOL, NL, B, c, hkv, d), device="cuda", generator=gen).to(bf).view(torch.int16)
+    qpool = torch.randn((POOL, NL, B, c, hq, d), device="cuda", generator=gen).to(bf).view(torch.int16)
+    outs = torch.empty((NL, B, c, hq, d), device="cuda", dtype=torch.int16)
+    ptr = lambda t: t.data_ptr()
+    k_ptrs = [[ptr(kpool[i, l]) for l in range(NL)] for i in range(POOL)]
+    v_ptrs = [[ptr(vpool[i, l]) for l in range(NL)] for i in range(POOL)]
+    q_ptrs = [[ptr(qpool[i, l]) for l in range(NL)] for i in range(POOL)]
+    o_ptrs = [ptr(outs[l]) for l in range(NL)]
+    h = cache.handle
+    L = a8r.lib()
+
+    def step(i, timers=None):
+        kp, vp, qp = k_ptrs[i % POOL], v_ptrs[i % POOL], q_ptrs[i % POOL]
+        for layer in range(NL):
+            st = L.a8r_append_kv(h, layer, 0, B, c, kp[layer], vp[layer], None, None)
+            if timers is not None:
+                timers[layer][0].record(stream)
+            if c == 1:
+                st |= L.a8r_decode_attn(h, layer, 0, B, qp[layer], o_ptrs[layer])
+            else:
+                st |= L.a8r_chunk_attn(h, layer, 0, B, c, qp[layer], o_ptrs[layer])
+            if timers is not None:
+                timers[layer][1].record(stream)
+            if st:
+                raise a8r.A8RError(st, L.a8r_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    steps_per_s = 1000.0 / ms
+
+    # per-launch duration of the attention kernel(s): events around every
+    # attention call of a second pass over the same number of steps
+    n_t = min(args.steps, 200)
+    timers = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(NL)] for _ in range(n_t)]
+    for i in range(n_t):
+        step(i, [[a, b] for a, b in timers[i]])
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for row in timers for a, b in row]
+    attn_ms = float(np.mean(durs))
+
+    live = w  # every stream holds a full window after pre-fill
+    bytes_launch = algorithmic_bytes(wl, live)
+    bytes_step = NL * (bytes_launch + append_bytes(wl))
+    gbps_step = bytes_step * steps_per_s / 1e9
+    achieved = bytes_launch / (attn_ms * 1e-3) / 1e9
+    flops_launch = attention_flops(wl, live)
+    traffic = traffic_from_profiles(args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": NL, "streams": B, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": d, "window": w, "positions_per_step": c,
+                   "start_positions": "seeded U[0,1e6)" if c == 1 else "seeded U[2^24-W,2^24)"},
+        "kv_gbps": round(gbps_step, 1),
+        "hbm_frac_step": round(gbps_step / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": bytes_step,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "a8r_decode_attn" if c == 1 else "a8r_chunk_attn",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": bytes_launch,
+            "avg_launch_ms": round(attn_ms, 5),
+            "mfma_tflops": round(flops_launch / (attn_ms * 1e-3) / 1e12, 2),
+            "mfma_frac_bf16_dense": round(flops_launch / (attn_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+    cache.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,66 @@
+// Internal definitions shared by the host side (a8r_host.cpp) and the HIP
+// kernels (a8r_kernels.hip).  Not part of the public ABI.
+//
+// Device memory layout of one cache (all regions 256-byte aligned):
+//   K ring  [n_layers][n_streams][n_kv_heads][W_pad][D]        row per slot
+//   V ring  [n_layers][n_streams][n_kv_heads][W_pad/8][D][8]   8-slot blocks,
+//            transposed inside a block so 8 consecutive slots of one dim are
+//            16 contiguous bytes (the k-operand layout of the PV MFMA)
+//   table   [W + 32][D/2] float2: (cos, sin)(r * theta^(-2i/D)) for r < W + 32,
+//            built in float64 on the host and rounded once to float32
+//   state   [n_layers][n_streams] DevState
+//   scratch split partials: O [rows][D] float32 and (m, l) [rows][2] float32
+// W_pad = W rounded up to a multiple of 32 (one MFMA key tile); padding slots
+// are zeroed at creation and never written, and never taken as live.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace a8r {
+
+constexpr int kTile = 32;          // keys per MFMA tile (4 aligned 8-slot V blocks)
+constexpr int kTablePad = 32;      // extra table rows beyond W
+constexpr int kMaxSplits = 16;     // most key splits per (stream, KV head)
+constexpr int kMaxPartialQ = 16;   // chunk sizes above this run without splits
+constexpr size_t kAlign = 256;
+
+struct DevState {
+    int64_t next_pos;   // absolute position of the next token
+    int32_t length;     // live tokens, <= W
+    int32_t next_slot;  // slot of the next token
+};
+
+// Everything a kernel needs to find a (layer, stream, kv head) window.
+struct Geometry {
+    void* k_ring;
+    void* v_ring;
+    const float2* table;
+    DevState* state;
+    float* part_o;      // split partials: [n_streams][n_kv_heads][kMaxSplits][rows_max][D]
+    float* part_ml;     // [n_streams][n_kv_heads][kMaxSplits][rows_max][2]
+    int n_layers, n_streams, hq, hkv, group, d, window, w_pad;
+    int elem_bytes;     // 2 (bf16) or 4 (f32)
+    int rows_max;       // max(1, min(max_chunk, kMaxPartialQ)) * group
+    float scale_log2;   // softmax scale * log2(e): scores are kept in base-2 units
+};
+
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__host__ __device__ inline int64_t pair_index(const Geometry& g, int layer, int b, int kh) {
+    return ((int64_t)layer * g.n_streams + b) * g.hkv + kh;
+}
+
+// ---- launchers (a8r_kernels.hip); each returns the hipError_t of its launch
+hipError_t launch_reset(const Geometry& g, int b0, int nb, const int64_t* next_pos,
+                        const int32_t* next_slot, hipStream_t s);
+hipError_t launch_append(const Geometry& g, int layer, int b0, int nb, int n_new,
+                         const void* k, const void* v, hipStream_t s);
+// Attention for n_q queries (1 = decode) per stream; picks a kernel and split count.
+hipError_t launch_attention(const Geometry& g, int layer, int b0, int nb, int n_q,
+                            const void* q, void* out, bool allow_mfma, int n_cu,
+                            hipStream_t s);
+
+}  // namespace a8r
