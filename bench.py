@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="qwen3b_batch64", choices=["qwen3b_batch64", "qwen3b_chunk8"])
+    ap.add_argument("--path", default="fused", choices=["fused", "separate"],
+                    help="decode step per layer as one a8r_append_decode_attn call (fused) or as "
+                         "a8r_append_kv + a8r_decode_attn (separate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
@@ -174,16 +177,24 @@ def main():
     h = cache.handle
     L = a8r.lib()
 
+    fused = c == 1 and args.path == "fused"
+
     def step(i, timers=None):
         kp, vp, qp = k_ptrs[i % POOL], v_ptrs[i % POOL], q_ptrs[i % POOL]
         for layer in range(NL):
-            st = L.a8r_append_kv(h, layer, 0, B, c, kp[layer], vp[layer], None, None)
-            if timers is not None:
-                timers[layer][0].record(stream)
-            if c == 1:
-                st |= L.a8r_decode_attn(h, layer, 0, B, qp[layer], o_ptrs[layer])
+            if fused:
+                if timers is not None:
+                    timers[layer][0].record(stream)
+                st = L.a8r_append_decode_attn(h, layer, 0, B, kp[layer], vp[layer], qp[layer], o_ptrs[layer],
+                                              None, None)
             else:
-                st |= L.a8r_chunk_attn(h, layer, 0, B, c, qp[layer], o_ptrs[layer])
+                st = L.a8r_append_kv(h, layer, 0, B, c, kp[layer], vp[layer], None, None)
+                if timers is not None:
+                    timers[layer][0].record(stream)
+                if c == 1:
+                    st |= L.a8r_decode_attn(h, layer, 0, B, qp[layer], o_ptrs[layer])
+                else:
+                    st |= L.a8r_chunk_attn(h, layer, 0, B, c, qp[layer], o_ptrs[layer])
             if timers is not None:
                 timers[layer][1].record(stream)
             if st:
@@ -241,7 +252,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "layers": NL, "streams": B, "q_heads": hq, "kv_heads": hkv,
+        "config": {"workload": wl.name, "path": "fused" if fused else "separate", "layers": NL, "streams": B, "q_heads": hq, "kv_heads": hkv,
                    "head_dim": d, "window": w, "positions_per_step": c,
                    "start_positions": "seeded U[0,1e6)" if c == 1 else "seeded U[2^24-W,2^24)"},
         "kv_gbps": round(gbps_step, 1),
@@ -249,7 +260,8 @@ def main():
         "bytes_per_step": bytes_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "a8r_decode_attn" if c == 1 else "a8r_chunk_attn",
+            "kernel": ("a8r_append_decode_attn (decode_mfma, fused append)" if fused else
+                       "a8r_decode_attn" if c == 1 else "a8r_chunk_attn"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

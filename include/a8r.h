@@ -161,6 +161,18 @@ a8r_status a8r_decode_attn(a8r_cache* cache, int32_t layer, int32_t b0, int32_t 
 a8r_status a8r_chunk_attn(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb,
                           int32_t n_new, const void* q, void* out);
 
+/* The decode step of an audio clock in one call: exactly a8r_append_kv with
+ * n_new = 1 followed by a8r_decode_attn on the same streams, executed as a
+ * single kernel (the new token's K/V are written into the ring by the same
+ * launch that attends to them).  k, v: device [nb][n_kv_heads][head_dim];
+ * q, out: device [nb][n_q_heads][head_dim]; slots_out / evicted_out as for
+ * a8r_append_kv (host, nb entries each, or NULL).  Shapes the fused kernel
+ * does not cover (float32, head groups above 16) run as the two calls.
+ * Errors: as a8r_append_kv and a8r_decode_attn; nothing changes on error. */
+a8r_status a8r_append_decode_attn(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb, const void* k,
+                                  const void* v, const void* q, void* out, int32_t* slots_out,
+                                  int64_t* evicted_out);
+
 /* Read the state of one (layer, stream) pair: next position P, live count L,
  * next slot S (host outputs, any may be NULL).  Synchronizes the stream and
  * checks the device-side copy against the host bookkeeping; a mismatch returns

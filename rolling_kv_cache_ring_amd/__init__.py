@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ENOMEM", 3: "EDEVICE", 4: "ESTATE", 5:
 
 EXPORTED = [
     "a8r_workspace_bytes", "a8r_cache_create", "a8r_cache_destroy", "a8r_set_stream", "a8r_reset",
-    "a8r_append_kv", "a8r_decode_attn", "a8r_chunk_attn", "a8r_get_state", "a8r_read_ring",
+    "a8r_append_kv", "a8r_decode_attn", "a8r_chunk_attn", "a8r_append_decode_attn",
+    "a8r_get_state", "a8r_read_ring",
     "a8r_last_error", "a8r_ledger_create", "a8r_ledger_destroy", "a8r_ledger_reset",
     "a8r_ledger_append", "a8r_ledger_get", "a8r_version",
 ]
@@ -91,6 +92,9 @@ def lib():
     L.a8r_chunk_attn.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  _c_void_p, _c_void_p]
     L.a8r_chunk_attn.restype = st
+    L.a8r_append_decode_attn.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32p, _i64p]
+    L.a8r_append_decode_attn.restype = st
     L.a8r_get_state.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, _i64p, _i32p, _i32p]
     L.a8r_get_state.restype = st
     L.a8r_read_ring.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, _c_void_p, _c_void_p]
@@ -202,6 +206,19 @@ def chunk_attn(handle: int, layer: int, b0: int, nb: int, n_new: int, q, out) ->
     _check(lib().a8r_chunk_attn(handle, layer, b0, nb, n_new, _ptr(q), _ptr(out)))
 
 
+def append_decode_attn(handle: int, layer: int, b0: int, nb: int, k, v, q, out, want_bookkeeping=True):
+    """a8r_append_kv (one token per stream) + a8r_decode_attn in one launch."""
+    if want_bookkeeping:
+        slots = np.empty((nb, 1), dtype=np.int32)
+        ev = np.empty((nb, 1), dtype=np.int64)
+        _check(lib().a8r_append_decode_attn(handle, layer, b0, nb, _ptr(k), _ptr(v), _ptr(q), _ptr(out),
+                                            slots.ctypes.data_as(_i32p), ev.ctypes.data_as(_i64p)))
+        return slots, ev
+    _check(lib().a8r_append_decode_attn(handle, layer, b0, nb, _ptr(k), _ptr(v), _ptr(q), _ptr(out),
+                                        None, None))
+    return None, None
+
+
 def get_state(handle: int, layer: int, b: int) -> tuple[int, int, int]:
     p, n, s = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
     _check(lib().a8r_get_state(handle, layer, b, ctypes.byref(p), ctypes.byref(n), ctypes.byref(s)))
@@ -246,6 +263,9 @@ class Cache:
 
     def chunk_attn(self, layer, b0, nb, n_new, q, out):
         chunk_attn(self.handle, layer, b0, nb, n_new, q, out)
+
+    def append_decode_attn(self, layer, b0, nb, k, v, q, out, want_bookkeeping=True):
+        return append_decode_attn(self.handle, layer, b0, nb, k, v, q, out, want_bookkeeping)
 
     def get_state(self, layer, b):
         return get_state(self.handle, layer, b)

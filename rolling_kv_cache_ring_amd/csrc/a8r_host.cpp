@@ -20,6 +20,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <limits>
 #include <new>
 #include <string>
@@ -114,7 +115,7 @@ struct Ledger {
 };
 
 struct Layout {
-    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, total;
+    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, counter_off, total;
     int w_pad, rows_max;
 };
 
@@ -172,6 +173,8 @@ a8r_status compute_layout(const a8r_config* c, Layout* lay) {
     off = a8r::align_up(off + prow * c->head_dim * 4, a8r::kAlign);
     lay->part_ml_off = off;
     off = a8r::align_up(off + prow * 2 * 4, a8r::kAlign);
+    lay->counter_off = off;
+    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * sizeof(int), a8r::kAlign);
     lay->total = off;
     lay->w_pad = w_pad;
     lay->rows_max = rows_max;
@@ -302,6 +305,7 @@ a8r_status a8r_cache_create(const a8r_config* cfg, void* hip_stream, void* works
     g.state = (a8r::DevState*)(b + lay.state_off);
     g.part_o = (float*)(b + lay.part_o_off);
     g.part_ml = (float*)(b + lay.part_ml_off);
+    g.counters = (int*)(b + lay.counter_off);
     g.n_layers = cfg->n_layers;
     g.n_streams = cfg->n_streams;
     g.hq = cfg->n_q_heads;
@@ -344,6 +348,27 @@ a8r_status a8r_set_stream(a8r_cache* c, void* hip_stream) {
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Fills the launch-argument state of streams [b0, b0 + nb) of one layer from
+// the host bookkeeping.
+void fill_batch(const a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, a8r::StreamBatch* sb) {
+    sb->b0 = b0;
+    sb->nb = nb;
+    for (int32_t i = 0; i < nb; ++i) {
+        const PairState& p = c->ledger.at(layer, b0 + i);
+        sb->next_slot[i] = p.next_slot;
+        sb->length[i] = p.length;
+        sb->next_pos[i] = p.next_pos;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
 a8r_status a8r_reset(a8r_cache* c, int32_t b0, int32_t nb, const int64_t* next_pos, const int32_t* next_slot) {
     a8r_status st = check_live(c);
     if (st != A8R_OK) return st;
@@ -351,9 +376,13 @@ a8r_status a8r_reset(a8r_cache* c, int32_t b0, int32_t nb, const int64_t* next_p
     std::vector<int32_t> slots(nb);
     for (int32_t i = 0; i < nb; ++i)
         slots[i] = next_slot ? next_slot[i] : (int32_t)(next_pos[i] % c->cfg.window);
-    hipError_t e = a8r::launch_reset(c->geo, b0, nb, next_pos, slots.data(), c->stream);
-    if (e != hipSuccess) return device_fail(c, e, "reset kernel");
     c->ledger.reset(b0, nb, next_pos, slots.data());
+    for (int32_t i0 = 0; i0 < nb; i0 += a8r::kBatch) {
+        a8r::StreamBatch sb;
+        fill_batch(c, 0, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
+        hipError_t e = a8r::launch_reset(c->geo, sb, c->stream);
+        if (e != hipSuccess) return device_fail(c, e, "reset kernel");
+    }
     return ok();
 }
 
@@ -365,14 +394,20 @@ a8r_status a8r_append_kv(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, in
     if (n_new > c->cfg.max_chunk) return fail(A8R_EINVAL, "n_new %d > max_chunk %d", n_new, c->cfg.max_chunk);
     if (!k || !v) return fail(A8R_EINVAL, "k or v is NULL");
     if (!aligned16(k) || !aligned16(v)) return fail(A8R_EINVAL, "k and v must be 16-byte aligned");
-    hipError_t e = a8r::launch_append(c->geo, layer, b0, nb, n_new, k, v, c->stream);
-    if (e != hipSuccess) return device_fail(c, e, "append kernel");
+    const size_t row = (size_t)n_new * c->cfg.n_kv_heads * c->cfg.head_dim * c->geo.elem_bytes;
+    for (int32_t i0 = 0; i0 < nb; i0 += a8r::kBatch) {
+        a8r::StreamBatch sb;
+        fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
+        hipError_t e = a8r::launch_append(c->geo, layer, sb, n_new, (const uint8_t*)k + i0 * row,
+                                          (const uint8_t*)v + i0 * row, c->stream);
+        if (e != hipSuccess) return device_fail(c, e, "append kernel");
+    }
     c->ledger.append(layer, b0, nb, n_new, slots_out, evicted_out);
     return ok();
 }
 
-static a8r_status attention_call(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_q, const void* q,
-                                  void* out) {
+static a8r_status check_attention(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_q, int32_t added,
+                                  const void* q, void* out) {
     a8r_status st = check_live(c);
     if (st != A8R_OK) return st;
     if ((st = check_streams(c, layer, b0, nb)) != A8R_OK) return st;
@@ -381,14 +416,27 @@ static a8r_status attention_call(a8r_cache* c, int32_t layer, int32_t b0, int32_
     if (!q || !out) return fail(A8R_EINVAL, "q or out is NULL");
     if (!aligned16(q) || !aligned16(out)) return fail(A8R_EINVAL, "q and out must be 16-byte aligned");
     for (int32_t i = 0; i < nb; ++i) {
-        const int32_t len = c->ledger.at(layer, b0 + i).length;
+        const int32_t len = std::min(c->ledger.at(layer, b0 + i).length + added, c->cfg.window);
         if (len < n_q)
             return fail(A8R_ESTATE, "stream %d layer %d holds %d live tokens, need >= %d", b0 + i, layer, len,
                         n_q);
     }
-    hipError_t e = a8r::launch_attention(c->geo, layer, b0, nb, n_q, q, out,
-                                         c->cfg.kernel_policy == A8R_KERNELS_AUTO, c->n_cu, c->stream);
-    if (e != hipSuccess) return device_fail(c, e, "attention kernel");
+    return A8R_OK;
+}
+
+static a8r_status attention_call(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_q, const void* q,
+                                  void* out) {
+    a8r_status st = check_attention(c, layer, b0, nb, n_q, 0, q, out);
+    if (st != A8R_OK) return st;
+    const size_t qrow = (size_t)n_q * c->cfg.n_q_heads * c->cfg.head_dim * c->geo.elem_bytes;
+    for (int32_t i0 = 0; i0 < nb; i0 += a8r::kBatch) {
+        a8r::StreamBatch sb;
+        fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
+        hipError_t e = a8r::launch_attention(c->geo, layer, sb, n_q, (const uint8_t*)q + i0 * qrow,
+                                             (uint8_t*)out + i0 * qrow, c->cfg.kernel_policy == A8R_KERNELS_AUTO,
+                                             c->n_cu, c->stream);
+        if (e != hipSuccess) return device_fail(c, e, "attention kernel");
+    }
     return ok();
 }
 
@@ -399,6 +447,30 @@ a8r_status a8r_decode_attn(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, 
 a8r_status a8r_chunk_attn(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_new, const void* q,
                           void* out) {
     return attention_call(c, layer, b0, nb, n_new, q, out);
+}
+
+a8r_status a8r_append_decode_attn(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, const void* k,
+                                  const void* v, const void* q, void* out, int32_t* slots_out,
+                                  int64_t* evicted_out) {
+    a8r_status st = check_live(c);
+    if (st != A8R_OK) return st;
+    if ((st = c->ledger.check_append(layer, b0, nb, 1)) != A8R_OK) return st;
+    if (!k || !v) return fail(A8R_EINVAL, "k or v is NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(A8R_EINVAL, "k and v must be 16-byte aligned");
+    if ((st = check_attention(c, layer, b0, nb, 1, 1, q, out)) != A8R_OK) return st;
+    const size_t kvrow = (size_t)c->cfg.n_kv_heads * c->cfg.head_dim * c->geo.elem_bytes;
+    const size_t qrow = (size_t)c->cfg.n_q_heads * c->cfg.head_dim * c->geo.elem_bytes;
+    for (int32_t i0 = 0; i0 < nb; i0 += a8r::kBatch) {
+        a8r::StreamBatch sb;
+        fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
+        hipError_t e = a8r::launch_append_decode(c->geo, layer, sb, (const uint8_t*)k + i0 * kvrow,
+                                                 (const uint8_t*)v + i0 * kvrow, (const uint8_t*)q + i0 * qrow,
+                                                 (uint8_t*)out + i0 * qrow,
+                                                 c->cfg.kernel_policy == A8R_KERNELS_AUTO, c->n_cu, c->stream);
+        if (e != hipSuccess) return device_fail(c, e, "append+decode kernel");
+    }
+    c->ledger.append(layer, b0, nb, 1, slots_out, evicted_out);
+    return ok();
 }
 
 a8r_status a8r_get_state(a8r_cache* c, int32_t layer, int32_t b, int64_t* next_pos, int32_t* length,

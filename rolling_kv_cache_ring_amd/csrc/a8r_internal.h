@@ -8,8 +8,13 @@
 //            16 contiguous bytes (the k-operand layout of the PV MFMA)
 //   table   [W + 32][D/2] float2: (cos, sin)(r * theta^(-2i/D)) for r < W + 32,
 //            built in float64 on the host and rounded once to float32
-//   state   [n_layers][n_streams] DevState
-//   scratch split partials: O [rows][D] float32 and (m, l) [rows][2] float32
+//   state   [n_layers][n_streams] DevState: a device-side record of every
+//            pair's (P, L, S), written by the reset / append kernels and read
+//            back only by a8r_get_state to cross-check the host bookkeeping.
+//            Kernels take the state they work on from their launch arguments
+//            (StreamBatch), filled from the host bookkeeping at call time.
+//   scratch split partials: O [rows][D] float32 and (m, l) [rows][2] float32,
+//            and one arrival counter per (stream, KV head), zero between calls
 // W_pad = W rounded up to a multiple of 32 (one MFMA key tile); padding slots
 // are zeroed at creation and never written, and never taken as live.
 #pragma once
@@ -26,11 +31,21 @@ constexpr int kTablePad = 32;      // extra table rows beyond W
 constexpr int kMaxSplits = 16;     // most key splits per (stream, KV head)
 constexpr int kMaxPartialQ = 16;   // chunk sizes above this run without splits
 constexpr size_t kAlign = 256;
+constexpr int kBatch = 128;        // streams per launch (their state travels in the arguments)
 
 struct DevState {
     int64_t next_pos;   // absolute position of the next token
     int32_t length;     // live tokens, <= W
     int32_t next_slot;  // slot of the next token
+};
+
+// State of up to kBatch consecutive streams [b0, b0 + nb) of one layer, as the
+// host bookkeeping holds it when the call is made.
+struct StreamBatch {
+    int b0, nb;
+    int32_t next_slot[kBatch];
+    int32_t length[kBatch];
+    int64_t next_pos[kBatch];
 };
 
 // Everything a kernel needs to find a (layer, stream, kv head) window.
@@ -41,6 +56,7 @@ struct Geometry {
     DevState* state;
     float* part_o;      // split partials: [n_streams][n_kv_heads][kMaxSplits][rows_max][D]
     float* part_ml;     // [n_streams][n_kv_heads][kMaxSplits][rows_max][2]
+    int* counters;      // [n_streams][n_kv_heads] split arrival counters, 0 between calls
     int n_layers, n_streams, hq, hkv, group, d, window, w_pad;
     int elem_bytes;     // 2 (bf16) or 4 (f32)
     int rows_max;       // max(1, min(max_chunk, kMaxPartialQ)) * group
@@ -53,14 +69,20 @@ __host__ __device__ inline int64_t pair_index(const Geometry& g, int layer, int 
     return ((int64_t)layer * g.n_streams + b) * g.hkv + kh;
 }
 
-// ---- launchers (a8r_kernels.hip); each returns the hipError_t of its launch
-hipError_t launch_reset(const Geometry& g, int b0, int nb, const int64_t* next_pos,
-                        const int32_t* next_slot, hipStream_t s);
-hipError_t launch_append(const Geometry& g, int layer, int b0, int nb, int n_new,
+// ---- launchers (a8r_kernels.hip); each returns the hipError_t of its launch.
+// Device pointers k, v, q, out point at the batch's first stream.
+// Writes the device state record of every layer for a batch of reset streams.
+hipError_t launch_reset(const Geometry& g, const StreamBatch& after, hipStream_t s);
+// Copies n_new tokens per stream into the ring; `before` is the state before.
+hipError_t launch_append(const Geometry& g, int layer, const StreamBatch& before, int n_new,
                          const void* k, const void* v, hipStream_t s);
-// Attention for n_q queries (1 = decode) per stream; picks a kernel and split count.
-hipError_t launch_attention(const Geometry& g, int layer, int b0, int nb, int n_q,
-                            const void* q, void* out, bool allow_mfma, int n_cu,
-                            hipStream_t s);
+// Attention for n_q queries (1 = decode) per stream; `now` is the current state.
+hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now, int n_q,
+                            const void* q, void* out, bool allow_mfma, int n_cu, hipStream_t s);
+// One new token per stream appended and attended in one launch where the MFMA
+// decode kernel applies (else append + attention); `before` is the state before.
+hipError_t launch_append_decode(const Geometry& g, int layer, const StreamBatch& before,
+                                const void* k, const void* v, const void* q, void* out,
+                                bool allow_mfma, int n_cu, hipStream_t s);
 
 }  // namespace a8r

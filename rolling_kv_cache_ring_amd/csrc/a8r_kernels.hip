@@ -10,20 +10,25 @@
 // the stored K/V bits are never rewritten.
 //
 // Kernels:
-//   reset_kernel       device copy of the per-pair state after a reset
-//   append_kernel      copies new K/V rows into their ring slots and advances
-//                      the device state (one block per stream)
+//   reset_kernel       device record of the per-pair state after a reset
+//   append_kernel      copies new K/V rows into their ring slots (one block per
+//                      stream) and records the new state
 //   attn_portable      any dtype / group size / chunk size; LDS-tiled VALU
-//   decode_mfma        bf16 decode, QK^T and PV on v_mfma_f32_16x16x32_bf16
-//   combine_kernel     merges split-K partials {m, l, O} into the output
+//   combine_kernel     merges split-K partials {m, l, O} of attn_portable
+//   decode_mfma        bf16 decode (optionally fused with the append of the
+//                      new token); QK^T and PV on v_mfma_f32_16x16x32_bf16,
+//                      split-K partials merged by the last block to finish
 //
-// Scores are kept in base-2 units (the softmax scale is multiplied by log2 e
-// and folded into the query) so every exponential is one v_exp_f32.
+// Every kernel takes the ring state of its streams from its launch arguments
+// (StreamBatch, filled by the host from its bookkeeping when the call is made).
+// Scores are kept in base-2 units (the softmax scale is multiplied by log2 e)
+// so every exponential is one v_exp_f32.
 
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "a8r_internal.h"
 
@@ -64,83 +69,70 @@ __device__ __forceinline__ void store_elem(void* base, int64_t i, float x) {
     }
 }
 
-__device__ __forceinline__ DevState load_state(const Geometry& g, int layer, int b) {
-    return g.state[(int64_t)layer * g.n_streams + b];
-}
-
-__device__ __forceinline__ int oldest_slot(const DevState& st, int w) {
-    int o = st.next_slot - st.length;
-    return o < 0 ? o + w : o;
-}
+__device__ __forceinline__ int wrap_slot(int s, int w) { return s >= w ? s - w : s; }
 
 // ---------------------------------------------------------------- reset ----
-constexpr int kResetBatch = 128;
-struct ResetBatch {
-    int b0, nb;
-    int64_t pos[kResetBatch];
-    int32_t slot[kResetBatch];
-};
-
-__global__ void reset_kernel(Geometry g, ResetBatch r) {
+__global__ void reset_kernel(Geometry g, StreamBatch r) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= g.n_layers * r.nb) return;
     const int layer = t / r.nb, i = t - layer * r.nb;
     DevState s;
-    s.next_pos = r.pos[i];
-    s.length = 0;
-    s.next_slot = r.slot[i];
+    s.next_pos = r.next_pos[i];
+    s.length = r.length[i];
+    s.next_slot = r.next_slot[i];
     g.state[(int64_t)layer * g.n_streams + r.b0 + i] = s;
 }
 
 // --------------------------------------------------------------- append ----
-// One block per stream: every thread reads the stream's state, the block copies
-// n_new x Hkv rows (16 bytes per thread step) into K rows and the transposed V
-// blocks, then thread 0 advances the state.  Slot of token j = (S + j) mod W.
+// Writes one 16-byte chunk c of a token row of K and V into ring slot `slot`:
+// K rows are row-major; element d of V for slot s lives at ((s/8)*D + d)*8 + s%8
+// of the head's V block array.
 template <int EB>
-__global__ __launch_bounds__(256) void append_kernel(Geometry g, int layer, int b0, int n_new,
+__device__ __forceinline__ void write_token(const Geometry& g, int64_t pair, int slot, int c,
+                                            const uint8_t* ksrc, const uint8_t* vsrc) {
+    constexpr int per16 = 16 / EB;
+    const int D = g.d;
+    uint8_t* kdst = (uint8_t*)g.k_ring + ((pair * g.w_pad + slot) * D + (int64_t)c * per16) * EB;
+    *(u32x4*)kdst = *(const u32x4*)ksrc;
+    const u32x4 vv = *(const u32x4*)vsrc;
+    uint8_t* vblk = (uint8_t*)g.v_ring + ((pair * (g.w_pad / 8) + slot / 8) * (int64_t)D * 8) * EB;
+    const int lane8 = slot & 7;
+#pragma unroll
+    for (int u = 0; u < per16; ++u) {
+        const int d = c * per16 + u;
+        if constexpr (EB == 2) {
+            const uint32_t w = vv[u >> 1];
+            ((uint16_t*)vblk)[(int64_t)d * 8 + lane8] = (uint16_t)((u & 1) ? (w >> 16) : (w & 0xffffu));
+        } else {
+            ((uint32_t*)vblk)[(int64_t)d * 8 + lane8] = vv[u];
+        }
+    }
+}
+
+// One block per stream; token j of stream b goes to slot (S + j) mod W.
+template <int EB>
+__global__ __launch_bounds__(256) void append_kernel(Geometry g, int layer, StreamBatch st, int n_new,
                                                      const uint8_t* __restrict__ k,
                                                      const uint8_t* __restrict__ v) {
-    const int bi = blockIdx.x, b = b0 + bi;
-    DevState* sp = g.state + (int64_t)layer * g.n_streams + b;
-    const DevState st = *sp;
+    const int bi = blockIdx.x, b = st.b0 + bi;
     const int D = g.d, W = g.window;
-    constexpr int per16 = 16 / EB;             // elements per 16-byte chunk
+    constexpr int per16 = 16 / EB;
     const int chunks = D / per16;
     const int total = n_new * g.hkv * chunks;
+    const int s0 = st.next_slot[bi];
     for (int t = threadIdx.x; t < total; t += blockDim.x) {
         const int c = t % chunks;
         const int rest = t / chunks;
         const int kh = rest % g.hkv, j = rest / g.hkv;
-        int slot = st.next_slot + j;
-        if (slot >= W) slot -= W;
         const int64_t src = ((((int64_t)bi * n_new + j) * g.hkv + kh) * D + (int64_t)c * per16) * EB;
-        const int64_t pair = pair_index(g, layer, b, kh);
-        // K: row-major row of this slot
-        uint8_t* kdst = (uint8_t*)g.k_ring + ((pair * g.w_pad + slot) * D + (int64_t)c * per16) * EB;
-        *(u32x4*)kdst = *(const u32x4*)(k + src);
-        // V: element d of slot s lives at ((s/8)*D + d)*8 + s%8
-        const u32x4 vv = *(const u32x4*)(v + src);
-        uint8_t* vblk = (uint8_t*)g.v_ring + ((pair * (g.w_pad / 8) + slot / 8) * (int64_t)D * 8) * EB;
-        const int lane8 = slot & 7;
-#pragma unroll
-        for (int u = 0; u < per16; ++u) {
-            const int d = c * per16 + u;
-            if constexpr (EB == 2) {
-                const uint32_t w = vv[u >> 1];
-                ((uint16_t*)vblk)[(int64_t)d * 8 + lane8] = (uint16_t)((u & 1) ? (w >> 16) : (w & 0xffffu));
-            } else {
-                ((uint32_t*)vblk)[(int64_t)d * 8 + lane8] = vv[u];
-            }
-        }
+        write_token<EB>(g, pair_index(g, layer, b, kh), wrap_slot(s0 + j, W), c, k + src, v + src);
     }
-    __syncthreads();
     if (threadIdx.x == 0) {
-        DevState ns = st;
-        ns.next_pos = st.next_pos + n_new;
-        ns.length = st.length + n_new > W ? W : st.length + n_new;
-        int s = st.next_slot + n_new;
-        ns.next_slot = s >= W ? s - W : s;
-        *sp = ns;
+        DevState ns;
+        ns.next_pos = st.next_pos[bi] + n_new;
+        ns.length = min(st.length[bi] + n_new, W);
+        ns.next_slot = wrap_slot(s0 + n_new, W);
+        g.state[(int64_t)layer * g.n_streams + b] = ns;
     }
 }
 
@@ -178,7 +170,7 @@ __global__ __launch_bounds__(128) void combine_kernel(Geometry g, int n_q, int n
 // on VALU with 4 threads per row (4 keys of the tile each for the scores, a
 // quarter of the head dims each for PV).
 template <int D, int EB>
-__global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, int b0, int n_q,
+__global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, StreamBatch st, int n_q,
                                                      const void* __restrict__ q,
                                                      void* __restrict__ out, int n_split) {
     constexpr int KT = 16, RG = 64, NP = D / 2, DQ = D / 4;
@@ -189,10 +181,11 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, int 
     const int tid = threadIdx.x;
     const int bi = blockIdx.z, kh = blockIdx.y;
     const int split = blockIdx.x % n_split, rg = blockIdx.x / n_split;
-    const int b = b0 + bi, G = g.group, W = g.window;
+    const int b = st.b0 + bi, G = g.group, W = g.window;
     const int rows = n_q * G, row0 = rg * RG;
-    const DevState st = load_state(g, layer, b);
-    const int L = st.length, oldest = oldest_slot(st, W);
+    const int L = st.length[bi];
+    int oldest = st.next_slot[bi] - L;
+    if (oldest < 0) oldest += W;
     const int64_t pair = pair_index(g, layer, b, kh);
     const void* kring = (const uint8_t*)g.k_ring + pair * g.w_pad * D * EB;
     const void* vring = (const uint8_t*)g.v_ring + pair * g.w_pad * D * EB;
@@ -233,8 +226,7 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, int 
             const int j = idx / NP, i = idx - j * NP, r = kt * KT + j;
             float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
             if (r < L) {
-                int slot = oldest + r;
-                if (slot >= W) slot -= W;
+                const int slot = wrap_slot(oldest + r, W);
                 const float x1 = load_elem<EB>(kring, (int64_t)slot * D + i);
                 const float x2 = load_elem<EB>(kring, (int64_t)slot * D + i + NP);
                 const float2 cs = g.table[(int64_t)r * NP + i];
@@ -311,10 +303,12 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, int 
 //
 // Rotation: with R(x) the split-half rotation by index x, the score is
 // <R(r_q) q, R(rho + t) k> = <R(r_q - rho) q, R(t) k> because rotations in each
-// 2-D plane compose additively and are orthogonal.  So each lane rotates its
-// key rows by R(t) (t < 32, from LDS) and the query is rotated once per visit
-// by R(r_q - rho) (a table row < W + 32).  All coefficients come from the
-// float64-built table; no absolute position enters float arithmetic.
+// 2-D plane compose additively and are orthogonal.  Each lane always handles
+// the same two key offsets t of a tile, so its R(t) coefficients are loaded
+// once and kept in registers; the query is rotated once per visit by
+// R(r_q - rho) (a table row < W + 32) whose coefficients are fetched together
+// with the visit's K/V.  Every coefficient comes from the float64-built table;
+// no absolute position enters float arithmetic.
 //
 // MFMA mapping (v_mfma_f32_16x16x32_bf16, lane l = 16*gq + n):
 //   QK: S^T[key][head] = K_rot[key][dims] * Q_rot^T; A row n of tile half b is
@@ -323,57 +317,268 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, int 
 //   PV: O^T[d][head] = V^T[d][keys] * P^T; the A operand is 8 consecutive slots
 //       of one dim, i.e. 16 bytes of the transposed 8-slot V block.
 // Query heads beyond the group (n >= G) are zero rows and are discarded.
+//
+// Each wave keeps the next visit's loads in flight while it computes the
+// current one (two register buffers).  The splits of one (stream, KV head)
+// publish {m, l, O} partials with agent-coherent stores; the last block to
+// arrive (agent-scope atomic counter) merges them and re-arms the counter.
+//
+// Fused append: with k_new != nullptr the state in the arguments is the state
+// before the append, the window is the one after it, and the wave that owns
+// the new token's tile writes the token into its ring slot before it reads that
+// tile (no other wave touches that slot).
+
+// One wave's share of a visit, staged in LDS by direct global->LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16*l), so data in
+// flight holds no VGPRs.  Layout of one buffer: 2*(D/32) 1-KiB K chunks
+// (tile half b, dim chunk kk) then D/16 1-KiB V chunks; each lane reads back
+// exactly the 16 bytes it requested.
 template <int D>
-__device__ __forceinline__ void rotate_key_rows(const float2* __restrict__ coef, const u32x4 (&kr)[D / 32],
-                                                bf16x8 (&kb)[D / 32]) {
-    constexpr int KK = D / 32, HP = KK / 2;
+struct DecodeLds {
+    static constexpr int kChunks = 2 * (D / 32) + D / 16;
+    static constexpr int kBytes = kChunks * 1024;
+};
+
+template <int D>
+struct DecodeCoef {
+    float4 qc[D / 64][4];   // (cos, sin) pairs of R(r_q - rho) for this lane's query dims
+};
+
+struct DecodeCtx {
+    const uint16_t* kp;
+    const uint16_t* vp;
+    const float2* table;
+    int oldest, t_o, p0t, n_tiles, L, W, rq, tb0, tb1, gq, n;
+    float scale_log2;
+};
+
+__device__ __forceinline__ int visit_tile(const DecodeCtx& c, int k) {
+    const int p = c.p0t + k;
+    return p >= c.n_tiles ? p - c.n_tiles : p;
+}
+
+__device__ __forceinline__ int visit_rho(const DecodeCtx& c, int k, int s0) {
+    if (k == 0) return -c.t_o;
+    const int rho = s0 - c.oldest;
+    return rho < 0 ? rho + c.W : rho;
+}
+
+// (cos, sin) of the lane's 8*(D/64) pairs (dims 8*gq + 32*kk + e, kk < D/64)
+// of table row `row`.
+template <int D>
+__device__ __forceinline__ void load_coef(const float2* table, int row, int gq, float4 (&cf)[D / 64][4]) {
+    const float4* p = (const float4*)(table + (int64_t)row * (D / 2) + 8 * gq);
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cf[kk][j] = p[8 * kk + j];
+}
+
+// Rotates a lane's slice of a bf16 row (dims 8*gq + 32*kk + e) by the pairs in
+// cf: x_i, x_{i+D/2} -> x_i c - x_{i+D/2} s, x_{i+D/2} c + x_i s, rounded to bf16.
+template <int D>
+__device__ __forceinline__ void rotate_row(const float4 (&cf)[D / 64][4], const u32x4 (&x)[D / 32],
+                                           bf16x8 (&y)[D / 32]) {
+    constexpr int HP = D / 64;
 #pragma unroll
     for (int kk = 0; kk < HP; ++kk) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float2 cs = coef[32 * kk + e];
-            const uint32_t w1 = kr[kk][e >> 1], w2 = kr[kk + HP][e >> 1];
+            const float4 c4 = cf[kk][e >> 1];
+            const float cs_x = (e & 1) ? c4.z : c4.x, cs_y = (e & 1) ? c4.w : c4.y;
+            const uint32_t w1 = x[kk][e >> 1], w2 = x[kk + HP][e >> 1];
             const float x1 = (e & 1) ? hi_bf16(w1) : lo_bf16(w1);
             const float x2 = (e & 1) ? hi_bf16(w2) : lo_bf16(w2);
-            kb[kk][e] = (__bf16)(x1 * cs.x - x2 * cs.y);
-            kb[kk + HP][e] = (__bf16)(x2 * cs.x + x1 * cs.y);
+            y[kk][e] = (__bf16)(x1 * cs_x - x2 * cs_y);
+            y[kk + HP][e] = (__bf16)(x2 * cs_x + x1 * cs_y);
         }
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Issues every global load of a visit: K rows and V blocks into the wave's LDS
+// buffer `buf` (wave-uniform), the query rotation coefficients into registers.
 template <int D>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void decode_mfma(Geometry g, int layer, int b0,
+__device__ __forceinline__ void load_visit(const DecodeCtx& c, int k, unsigned char* buf, DecodeCoef<D>& t) {
+    constexpr int KK = D / 32, NB = D / 16;
+    const int p = visit_tile(c, k);
+    const int s0 = p * kTile;
+    const uint16_t* r0 = c.kp + (int64_t)(s0 + c.tb0) * D + 8 * c.gq;
+    const uint16_t* r1 = c.kp + (int64_t)(s0 + c.tb1) * D + 8 * c.gq;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        __builtin_amdgcn_global_load_lds((const void*)(r0 + 32 * kk), (lds_void*)(buf + kk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(r1 + 32 * kk), (lds_void*)(buf + (KK + kk) * 1024), 16, 0,
+                                         0);
+    }
+    const uint16_t* vb = c.vp + ((int64_t)(p * 4 + c.gq) * D + c.n) * 8;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)nb * 16 * 8),
+                                         (lds_void*)(buf + (2 * KK + nb) * 1024), 16, 0, 0);
+    load_coef<D>(c.table, c.rq - visit_rho(c, k, s0), c.gq, t.qc);
+}
+
+template <int D>
+__device__ __forceinline__ void compute_visit(const DecodeCtx& c, int k, const unsigned char* buf,
+                                              const DecodeCoef<D>& t, const u32x4 (&qraw)[D / 32],
+                                              const float4 (&cf0)[D / 64][4], const float4 (&cf1)[D / 64][4],
+                                              floatx4 (&o)[D / 16], float& m, float& l, int lane) {
+    constexpr int KK = D / 32, NB = D / 16;
+    const int p = visit_tile(c, k);
+    const int s0 = p * kTile;
+    const int rho = visit_rho(c, k, s0);
+    const u32x4* lb = (const u32x4*)buf + lane;        // this lane's 16 bytes of each 1-KiB chunk
+    bf16x8 qb[KK];
+    rotate_row<D>(t.qc, qraw, qb);            // query by R(r_q - rho)
+    // keys by R(t); on the first visit the caller has swapped in R(t + W) for the
+    // window's newest keys that share the oldest key's tile (index rho + t + W)
+    const bool seam = (k == 0) && (c.t_o > 0);
+    floatx4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+    {
+        u32x4 kr[KK];
+        bf16x8 kb[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kr[kk] = lb[kk * 64];
+        rotate_row<D>(cf0, kr, kb);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], sc0, 0, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kr[kk] = lb[(KK + kk) * 64];
+        rotate_row<D>(cf1, kr, kb);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], sc1, 0, 0, 0);
+    }
+    const float sl = c.scale_log2;
+    float s[8] = {sc0[0] * sl, sc0[1] * sl, sc0[2] * sl, sc0[3] * sl,
+                  sc1[0] * sl, sc1[1] * sl, sc1[2] * sl, sc1[3] * sl};
+    const bool full = (k != 0) && (rho + kTile <= c.L) && (s0 + kTile <= c.W);
+    if (!full) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int tt = 8 * c.gq + e;
+            int r = rho + tt;
+            if (seam && tt < c.t_o) r += c.W;
+            const bool ok = (r >= 0) && (r < c.L) && (s0 + tt < c.W);
+            if (!ok) s[e] = -INFINITY;
+        }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // lazy rescale: keep the running max unless a score exceeds it by 2^8
+    if (mx > m + 8.f) {
+        const float alpha = exp2f(m - mx);
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) o[i] *= alpha;
+        m = mx;
+    }
+    bf16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float pe = exp2f(s[e] - m);
+        l += pe;
+        pb[e] = (__bf16)pe;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const u32x4 vv = lb[(2 * KK + nb) * 64];
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[nb], 0, 0, 0);
+    }
+}
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, StreamBatch st,
                                                       const uint16_t* __restrict__ q,
-                                                      uint16_t* __restrict__ out, int n_split) {
-    constexpr int KK = D / 32, HP = KK / 2, NB = D / 16, NP = D / 2;
-    __shared__ float2 rt_lds[kTile * NP];          // R(t), t < 32
-    __shared__ float red_o[4][16][D];
+                                                      uint16_t* __restrict__ out, int n_split,
+                                                      const uint16_t* __restrict__ k_new,
+                                                      const uint16_t* __restrict__ v_new) {
+    constexpr int KK = D / 32, NB = D / 16;
+    constexpr int kBuf = DecodeLds<D>::kBytes;
+    constexpr int kLoadsPerVisit = DecodeLds<D>::kChunks + 4 * (D / 64);
+    // per wave two visit buffers, as two distinct LDS objects so that the
+    // compiler can tell the buffer being read from the one being filled; after
+    // the walk the first one holds the cross-wave merge (4 x 16 x D floats)
+    __shared__ __align__(16) unsigned char lds_tiles_a[4 * kBuf];
+    __shared__ __align__(16) unsigned char lds_tiles_b[4 * kBuf];
     __shared__ float red_ml[4][16][2];
+    __shared__ int s_last;
+    static_assert(4 * 16 * D * 4 <= 4 * kBuf, "merge buffer does not fit");
+    float (*red_o)[16][D] = (float (*)[16][D])lds_tiles_a;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, gq = lane >> 4;
     const int bi = blockIdx.z, kh = blockIdx.y, split = blockIdx.x;
-    const int b = b0 + bi, G = g.group, W = g.window;
+    const int b = st.b0 + bi, G = g.group, W = g.window;
+    const bool fused = k_new != nullptr;
+    unsigned char* buf_a = lds_tiles_a + wave * kBuf;
+    unsigned char* buf_b = lds_tiles_b + wave * kBuf;
 
-    for (int idx = tid; idx < kTile * NP; idx += 256) rt_lds[idx] = g.table[idx];
-
-    const DevState st = load_state(g, layer, b);
-    const int L = st.length, oldest = oldest_slot(st, W), rq = L - 1;
-    const int n_tiles = g.w_pad / kTile;
-    const int p0t = oldest / kTile, t_o = oldest - p0t * kTile;
+    // window after the (optional) append of one token
+    const int s_prev = st.next_slot[bi];
+    const int L = fused ? min(st.length[bi] + 1, W) : st.length[bi];
+    const int next_slot = fused ? wrap_slot(s_prev + 1, W) : s_prev;
+    DecodeCtx c;
+    c.L = L;
+    c.W = W;
+    c.oldest = next_slot - L < 0 ? next_slot - L + W : next_slot - L;
+    c.rq = L - 1;
+    c.n_tiles = g.w_pad / kTile;
+    c.p0t = c.oldest / kTile;
+    c.t_o = c.oldest - c.p0t * kTile;
+    c.tb0 = 8 * (n >> 2) + (n & 3);
+    c.tb1 = c.tb0 + 4;
+    c.gq = gq;
+    c.n = n;
+    c.scale_log2 = g.scale_log2;
+    c.table = g.table;
+    const int64_t pair = pair_index(g, layer, b, kh);
+    c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
+    c.vp = (const uint16_t*)g.v_ring + pair * g.w_pad * D;
     int n_visit;
     {
-        int last = oldest + L - 1;
+        int last = c.oldest + L - 1;
         if (last < W) {
-            n_visit = last / kTile - p0t + 1;
+            n_visit = last / kTile - c.p0t + 1;
         } else {
             last -= W;
-            n_visit = n_tiles - p0t + last / kTile + 1;
-            if (n_visit > n_tiles) n_visit = n_tiles;
+            n_visit = c.n_tiles - c.p0t + last / kTile + 1;
+            if (n_visit > c.n_tiles) n_visit = c.n_tiles;
         }
     }
     const int per = (n_visit + n_split - 1) / n_split;
     const int k0 = split * per, k1 = min(n_visit, k0 + per);
+
+    if (fused) {
+        // the wave whose visits include the new token's tile writes the token
+        int kv = s_prev / kTile - c.p0t;
+        if (kv < 0) kv += c.n_tiles;
+        if (kv >= k0 && kv < k1 && (kv - k0) % 4 == wave && lane < D / 8) {
+            const int64_t src = (((int64_t)bi * g.hkv + kh) * D + lane * 8) * 2;
+            write_token<2>(g, pair, s_prev, lane, (const uint8_t*)k_new + src, (const uint8_t*)v_new + src);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        if (kh == 0 && split == 0 && tid == 0) {
+            DevState ns;
+            ns.next_pos = st.next_pos[bi] + 1;
+            ns.length = L;
+            ns.next_slot = next_slot;
+            g.state[(int64_t)layer * g.n_streams + b] = ns;
+        }
+    }
+
+    // the first visit's loads go out before anything else
+    DecodeCoef<D> ca, cb;
+    int k = k0 + wave;
+    if (k < k1) load_visit<D>(c, k, buf_a, ca);
 
     // the query stays as bf16 bits (the softmax scale is applied to the scores)
     u32x4 qraw[KK];
@@ -385,119 +590,47 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void decode_mfma(Geometry g,
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qraw[kk] = u32x4{0u, 0u, 0u, 0u};
     }
-
-    const int tb0 = 8 * (n >> 2) + (n & 3), tb1 = tb0 + 4;
-    const int64_t pair = pair_index(g, layer, b, kh);
-    const uint16_t* kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
-    const uint16_t* vp = (const uint16_t*)g.v_ring + pair * g.w_pad * D;
+    // R(t) of the lane's two key offsets, resident for the whole walk; the wave
+    // that starts with the seam visit uses R(t + W) for offsets before the oldest
+    // slot until that visit is done
+    const bool seam_first = (k == 0) && (k < k1) && (c.t_o > 0);
+    float4 cf0[D / 64][4], cf1[D / 64][4];
+    load_coef<D>(g.table, seam_first && c.tb0 < c.t_o ? c.tb0 + W : c.tb0, gq, cf0);
+    load_coef<D>(g.table, seam_first && c.tb1 < c.t_o ? c.tb1 + W : c.tb1, gq, cf1);
 
     floatx4 o[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m = kNegBig, l = 0.f;
-    __syncthreads();
 
-    for (int k = k0 + wave; k < k1; k += 4) {
-        int p = p0t + k;
-        if (p >= n_tiles) p -= n_tiles;
-        const int s0 = p * kTile;
-        int rho;
-        if (k == 0) {
-            rho = -t_o;
-        } else {
-            rho = s0 - oldest;
-            if (rho < 0) rho += W;
+    // Software pipeline over this wave's visits k0 + wave, +4, ...: the loads of
+    // the next visit are issued before the current one is computed.  Past the
+    // last visit the prefetch re-reads the current tile (a cache hit) into the
+    // other buffer, so the number of loads in flight is the same every time.
+    while (k < k1) {
+        int kn = k + 4;
+        load_visit<D>(c, kn < k1 ? kn : k, buf_b, cb);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerVisit));   // visit k has landed
+        __builtin_amdgcn_sched_barrier(0);
+        compute_visit<D>(c, k, buf_a, ca, qraw, cf0, cf1, o, m, l, lane);
+        if (seam_first && k == 0) {          // back to R(t) after the seam visit
+            load_coef<D>(g.table, c.tb0, gq, cf0);
+            load_coef<D>(g.table, c.tb1, gq, cf1);
         }
-        u32x4 kr0[KK], kr1[KK], vr[NB];
-        {
-            const uint16_t* r0 = kp + (int64_t)(s0 + tb0) * D + 8 * gq;
-            const uint16_t* r1 = kp + (int64_t)(s0 + tb1) * D + 8 * gq;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                kr0[kk] = *(const u32x4*)(r0 + 32 * kk);
-                kr1[kk] = *(const u32x4*)(r1 + 32 * kk);
-            }
-            const uint16_t* vb = vp + ((int64_t)(p * 4 + gq) * D + n) * 8;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) vr[nb] = *(const u32x4*)(vb + (int64_t)nb * 16 * 8);
-        }
-        // query rotated by R(r_q - rho)
-        bf16x8 qb[KK];
-        {
-            const float2* ta = g.table + (int64_t)(rq - rho) * NP + 8 * gq;
-#pragma unroll
-            for (int kk = 0; kk < HP; ++kk) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float2 cs = ta[32 * kk + e];
-                    const uint32_t w1 = qraw[kk][e >> 1], w2 = qraw[kk + HP][e >> 1];
-                    const float x1 = (e & 1) ? hi_bf16(w1) : lo_bf16(w1);
-                    const float x2 = (e & 1) ? hi_bf16(w2) : lo_bf16(w2);
-                    qb[kk][e] = (__bf16)(x1 * cs.x - x2 * cs.y);
-                    qb[kk + HP][e] = (__bf16)(x2 * cs.x + x1 * cs.y);
-                }
-            }
-        }
-        // keys rotated by R(t) (or R(t + W) for the window's newest keys that
-        // share the oldest key's tile)
-        const bool seam = (k == 0) && (t_o > 0);
-        bf16x8 kb0[KK], kb1[KK];
-        if (!seam) {
-            rotate_key_rows<D>(rt_lds + tb0 * NP + 8 * gq, kr0, kb0);
-            rotate_key_rows<D>(rt_lds + tb1 * NP + 8 * gq, kr1, kb1);
-        } else {
-            const int row0 = tb0 < t_o ? tb0 + W : tb0;
-            const int row1 = tb1 < t_o ? tb1 + W : tb1;
-            rotate_key_rows<D>(g.table + (int64_t)row0 * NP + 8 * gq, kr0, kb0);
-            rotate_key_rows<D>(g.table + (int64_t)row1 * NP + 8 * gq, kr1, kb1);
-        }
-        floatx4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb0[kk], qb[kk], sc0, 0, 0, 0);
-            sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb1[kk], qb[kk], sc1, 0, 0, 0);
-        }
-        const float sl = g.scale_log2;
-        float s[8] = {sc0[0] * sl, sc0[1] * sl, sc0[2] * sl, sc0[3] * sl,
-                      sc1[0] * sl, sc1[1] * sl, sc1[2] * sl, sc1[3] * sl};
-        const bool full = (k != 0) && (rho + kTile <= L) && (s0 + kTile <= W);
-        if (!full) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = 8 * gq + e;
-                int r = rho + t;
-                if (seam && t < t_o) r += W;
-                const bool ok = (r >= 0) && (r < L) && (s0 + t < W);
-                if (!ok) s[e] = -INFINITY;
-            }
-        }
-        float mx = s[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // lazy rescale: keep the running max unless a score exceeds it by 2^8
-        if (mx > m + 8.f) {
-            const float alpha = exp2f(m - mx);
-            l *= alpha;
-#pragma unroll
-            for (int i = 0; i < NB; ++i) o[i] *= alpha;
-            m = mx;
-        }
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float pe = exp2f(s[e] - m);
-            l += pe;
-            pb[e] = (__bf16)pe;
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vr[nb]), pb, o[nb], 0, 0, 0);
+        k = kn;
+        if (k >= k1) break;
+        kn = k + 4;
+        load_visit<D>(c, kn < k1 ? kn : k, buf_a, ca);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerVisit));
+        __builtin_amdgcn_sched_barrier(0);
+        compute_visit<D>(c, k, buf_b, cb, qraw, cf0, cf1, o, m, l, lane);
+        k = kn;
     }
+    __builtin_amdgcn_s_waitcnt(0);   // the last prefetch lands before the LDS is reused
 
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    __syncthreads();
     if (n < G) {
         if (gq == 0) {
             red_ml[wave][n][0] = m;
@@ -524,82 +657,56 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void decode_mfma(Geometry g,
         if (n_split == 1) {
             out[((int64_t)bi * g.hq + kh * G + h) * D + d] = f32_to_bf16_bits(num / den);
         } else {
+            // agent-coherent stores: visible to the merging block on any XCD
+            // once they have completed, without a cache writeback
             const int64_t pr = part_row(g, bi, kh, split, h);
-            g.part_o[pr * D + d] = num;
+            __hip_atomic_store(&g.part_o[pr * D + d], num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (d == 0) {
-                g.part_ml[pr * 2] = mm;
-                g.part_ml[pr * 2 + 1] = den;
+                __hip_atomic_store(&g.part_ml[pr * 2], mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&g.part_ml[pr * 2 + 1], den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
-}
+    if (n_split == 1) return;
 
-int env_splits() {
-    static int v = -2;
-    if (v == -2) {
-        const char* s = getenv("A8R_DEBUG_SPLITS");
-        v = s ? atoi(s) : -1;
+    // wait until this thread's partial stores have completed, then count the
+    // block in; the last block of the pair merges every split's partials
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int* counter = &g.counters[bi * g.hkv + kh];
+    if (tid == 0) {
+        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == n_split - 1);
     }
-    return v;
-}
-
-}  // namespace
-
-// ================================================================ launchers ==
-hipError_t launch_reset(const Geometry& g, int b0, int nb, const int64_t* next_pos,
-                        const int32_t* next_slot, hipStream_t s) {
-    for (int i0 = 0; i0 < nb; i0 += kResetBatch) {
-        ResetBatch r;
-        r.b0 = b0 + i0;
-        r.nb = min(kResetBatch, nb - i0);
-        for (int i = 0; i < r.nb; ++i) {
-            r.pos[i] = next_pos[i0 + i];
-            r.slot[i] = next_slot[i0 + i];
+    __syncthreads();
+    if (!s_last) return;
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int h = idx / D, d = idx - h * D;
+        float mm = kNegBig;
+        for (int sp = 0; sp < n_split; ++sp)
+            mm = fmaxf(mm, __hip_atomic_load(&g.part_ml[part_row(g, bi, kh, sp, h) * 2], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+        float num = 0.f, den = 0.f;
+        for (int sp = 0; sp < n_split; ++sp) {
+            const int64_t pr = part_row(g, bi, kh, sp, h);
+            const float f =
+                exp2f(__hip_atomic_load(&g.part_ml[pr * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - mm);
+            den += f * __hip_atomic_load(&g.part_ml[pr * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            num += f * __hip_atomic_load(&g.part_o[pr * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        const int threads = g.n_layers * r.nb;
-        hipLaunchKernelGGL(reset_kernel, dim3((threads + 255) / 256), dim3(256), 0, s, g, r);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        out[((int64_t)bi * g.hq + kh * G + h) * D + d] = f32_to_bf16_bits(num / den);
     }
-    return hipSuccess;
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-hipError_t launch_append(const Geometry& g, int layer, int b0, int nb, int n_new, const void* k,
-                         const void* v, hipStream_t s) {
-    if (g.elem_bytes == 2)
-        hipLaunchKernelGGL(append_kernel<2>, dim3(nb), dim3(256), 0, s, g, layer, b0, n_new,
-                           (const uint8_t*)k, (const uint8_t*)v);
-    else
-        hipLaunchKernelGGL(append_kernel<4>, dim3(nb), dim3(256), 0, s, g, layer, b0, n_new,
-                           (const uint8_t*)k, (const uint8_t*)v);
-    return hipGetLastError();
+int env_int(const char* name, int dflt) {
+    const char* s = getenv(name);
+    return s ? atoi(s) : dflt;
 }
 
-namespace {
-
-template <int D, int EB>
-hipError_t run_portable(const Geometry& g, int layer, int b0, int nb, int n_q, const void* q,
-                        void* out, int n_split, hipStream_t s) {
-    const int rows = n_q * g.group;
-    const int n_rg = (rows + 63) / 64;
-    hipLaunchKernelGGL((attn_portable<D, EB>), dim3(n_split * n_rg, g.hkv, nb), dim3(256), 0, s, g,
-                       layer, b0, n_q, q, out, n_split);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || n_split == 1) return e;
-    hipLaunchKernelGGL((combine_kernel<D, EB>), dim3(nb * n_q * g.hq), dim3(D), 0, s, g, n_q, n_split,
-                       out);
-    return hipGetLastError();
-}
-
-template <int D>
-hipError_t run_decode_mfma(const Geometry& g, int layer, int b0, int nb, const void* q, void* out,
-                           int n_split, hipStream_t s) {
-    hipLaunchKernelGGL((decode_mfma<D>), dim3(n_split, g.hkv, nb), dim3(256), 0, s, g, layer, b0,
-                       (const uint16_t*)q, (uint16_t*)out, n_split);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || n_split == 1) return e;
-    hipLaunchKernelGGL((combine_kernel<D, 2>), dim3(nb * g.hq), dim3(D), 0, s, g, 1, n_split, out);
-    return hipGetLastError();
+int debug_splits() {
+    static const int v = env_int("A8R_DEBUG_SPLITS", -1);
+    return v;
 }
 
 int pick_splits(int pairs, int tiles, int target_blocks, int min_tiles_per_split) {
@@ -609,34 +716,91 @@ int pick_splits(int pairs, int tiles, int target_blocks, int min_tiles_per_split
     if (sp > cap) sp = cap;
     if (sp > kMaxSplits) sp = kMaxSplits;
     if (sp < 1) sp = 1;
+    if (debug_splits() > 0) sp = min(debug_splits(), kMaxSplits);
     return sp;
+}
+
+bool mfma_decode_ok(const Geometry& g) {
+    return g.elem_bytes == 2 && g.group <= 16 && (g.d == 64 || g.d == 128);
+}
+
+template <int D, int EB>
+hipError_t run_portable(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q,
+                        void* out, int n_split, hipStream_t s) {
+    const int rows = n_q * g.group;
+    const int n_rg = (rows + 63) / 64;
+    hipLaunchKernelGGL((attn_portable<D, EB>), dim3(n_split * n_rg, g.hkv, st.nb), dim3(256), 0, s, g,
+                       layer, st, n_q, q, out, n_split);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_split == 1) return e;
+    hipLaunchKernelGGL((combine_kernel<D, EB>), dim3(st.nb * n_q * g.hq), dim3(D), 0, s, g, n_q, n_split,
+                       out);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, const void* q, void* out,
+                           int n_cu, const void* k_new, const void* v_new, hipStream_t s) {
+    // one resident block per CU for D = 128 (one wave per SIMD), two for D = 64
+    const int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, D == 128 ? n_cu : 2 * n_cu, 4);
+    hipLaunchKernelGGL((decode_mfma<D>), dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st,
+                       (const uint16_t*)q, (uint16_t*)out, n_split, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention(const Geometry& g, int layer, int b0, int nb, int n_q, const void* q,
+// ================================================================ launchers ==
+hipError_t launch_reset(const Geometry& g, const StreamBatch& after, hipStream_t s) {
+    const int threads = g.n_layers * after.nb;
+    hipLaunchKernelGGL(reset_kernel, dim3((threads + 255) / 256), dim3(256), 0, s, g, after);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const Geometry& g, int layer, const StreamBatch& before, int n_new, const void* k,
+                         const void* v, hipStream_t s) {
+    if (g.elem_bytes == 2)
+        hipLaunchKernelGGL(append_kernel<2>, dim3(before.nb), dim3(256), 0, s, g, layer, before, n_new,
+                           (const uint8_t*)k, (const uint8_t*)v);
+    else
+        hipLaunchKernelGGL(append_kernel<4>, dim3(before.nb), dim3(256), 0, s, g, layer, before, n_new,
+                           (const uint8_t*)k, (const uint8_t*)v);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now, int n_q, const void* q,
                             void* out, bool allow_mfma, int n_cu, hipStream_t s) {
-    const int pairs = nb * g.hkv;
-    const int tiles = g.w_pad / kTile;
-    const bool mfma_decode = allow_mfma && n_q == 1 && g.elem_bytes == 2 && g.group <= 16 &&
-                             (g.d == 64 || g.d == 128);
-    if (mfma_decode) {
-        int sp = pick_splits(pairs, tiles, 2 * n_cu, 4);
-        if (env_splits() > 0) sp = min(env_splits(), kMaxSplits);
-        return g.d == 128 ? run_decode_mfma<128>(g, layer, b0, nb, q, out, sp, s)
-                          : run_decode_mfma<64>(g, layer, b0, nb, q, out, sp, s);
-    }
+    if (allow_mfma && n_q == 1 && mfma_decode_ok(g))
+        return g.d == 128 ? run_decode_mfma<128>(g, layer, now, q, out, n_cu, nullptr, nullptr, s)
+                          : run_decode_mfma<64>(g, layer, now, q, out, n_cu, nullptr, nullptr, s);
     int sp = 1;
     if (n_q <= kMaxPartialQ) {
         const int n_rg = (n_q * g.group + 63) / 64;
-        sp = pick_splits(pairs * n_rg, (g.w_pad + 15) / 16, 2 * n_cu, 2);
-        if (env_splits() > 0) sp = min(env_splits(), kMaxSplits);
+        sp = pick_splits(now.nb * g.hkv * n_rg, (g.w_pad + 15) / 16, 2 * n_cu, 2);
     }
     if (g.elem_bytes == 2)
-        return g.d == 128 ? run_portable<128, 2>(g, layer, b0, nb, n_q, q, out, sp, s)
-                          : run_portable<64, 2>(g, layer, b0, nb, n_q, q, out, sp, s);
-    return g.d == 128 ? run_portable<128, 4>(g, layer, b0, nb, n_q, q, out, sp, s)
-                      : run_portable<64, 4>(g, layer, b0, nb, n_q, q, out, sp, s);
+        return g.d == 128 ? run_portable<128, 2>(g, layer, now, n_q, q, out, sp, s)
+                          : run_portable<64, 2>(g, layer, now, n_q, q, out, sp, s);
+    return g.d == 128 ? run_portable<128, 4>(g, layer, now, n_q, q, out, sp, s)
+                      : run_portable<64, 4>(g, layer, now, n_q, q, out, sp, s);
+}
+
+hipError_t launch_append_decode(const Geometry& g, int layer, const StreamBatch& before, const void* k,
+                                const void* v, const void* q, void* out, bool allow_mfma, int n_cu,
+                                hipStream_t s) {
+    if (allow_mfma && mfma_decode_ok(g))
+        return g.d == 128 ? run_decode_mfma<128>(g, layer, before, q, out, n_cu, k, v, s)
+                          : run_decode_mfma<64>(g, layer, before, q, out, n_cu, k, v, s);
+    hipError_t e = launch_append(g, layer, before, 1, k, v, s);
+    if (e != hipSuccess) return e;
+    StreamBatch now = before;
+    for (int i = 0; i < now.nb; ++i) {
+        now.next_pos[i] += 1;
+        now.length[i] = min(now.length[i] + 1, g.window);
+        now.next_slot[i] = now.next_slot[i] + 1 == g.window ? 0 : now.next_slot[i] + 1;
+    }
+    return launch_attention(g, layer, now, 1, q, out, allow_mfma, n_cu, s);
 }
 
 }  // namespace a8r

@@ -55,6 +55,37 @@ def test_decode_stream_wraps(window, hq, hkv, d, bf16, portable):
 
 
 @pytest.mark.parametrize("portable", [False, True])
+@pytest.mark.parametrize("window,hq,hkv,d,bf16", [
+    (1, 8, 8, 64, True), (7, 16, 2, 128, True), (33, 16, 2, 128, True), (100, 8, 8, 64, True),
+    (64, 8, 8, 64, False), (96, 4, 1, 128, True), (256, 16, 2, 128, True),
+])
+def test_fused_append_decode_wraps(window, hq, hkv, d, bf16, portable):
+    """a8r_append_decode_attn equals append + decode, across fills and wraps,
+    mixed with separate appends and decodes on the same cache."""
+    say("fused_append_decode", window, hq, hkv, d, bf16, portable)
+    rng = np.random.default_rng(window * 7 + hq)
+    tw = Twin(2, 3, hq, hkv, d, window, 1, bf16, portable)
+    tw.reset(0, [5, 2**24 - 3, 77_777], [0, rng.integers(window), rng.integers(window)])
+    steps = 3 * window + 7
+    for t in range(steps):
+        layer = t % 2
+        k = rand(rng, 3, 1, hkv, d, bf16=bf16)
+        v = rand(rng, 3, 1, hkv, d, bf16=bf16)
+        q = rand(rng, 3, hq, d, bf16=bf16)
+        if t % 5 == 4:
+            tw.append(layer, 0, k, v)
+            tw.decode(layer, 0, q)
+        else:
+            tw.append_decode(layer, 0, k, v, q)
+    for layer in range(2):
+        for b in range(3):
+            tw.check_state(layer, b)
+            tw.check_ring(layer, b)
+    say("worst err", tw.worst)
+    tw.close()
+
+
+@pytest.mark.parametrize("portable", [False, True])
 @pytest.mark.parametrize("window,chunk,hq,hkv,d,bf16", [
     (64, 8, 16, 2, 128, True), (37, 5, 8, 8, 64, True), (16, 16, 16, 2, 128, True),
     (50, 3, 4, 2, 64, False), (128, 8, 16, 2, 128, True),

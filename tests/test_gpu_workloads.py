@@ -97,7 +97,7 @@ def test_qwen3b_single_100k_steps():
     _run_long_stream(wl, [0, wl.n_layers - 1], wl.steps, checks)
 
 
-def _full_size(wl, sampled_layers, sampled_streams, n_steps, chunk):
+def _full_size(wl, sampled_layers, sampled_streams, n_steps, chunk, fused=False):
     """Fill every (layer, stream) of the workload, then run batched steps as the
     benchmark does; compare the sampled pairs with the oracle."""
     import torch
@@ -154,12 +154,18 @@ def _full_size(wl, sampled_layers, sampled_streams, n_steps, chunk):
                     qj[b] = to_device(q, True)
                     host[b] = q
                     ora.append(layer, b, k[None], v[None])
-            slots, ev = cache.append_kv(layer, 0, B, chunk, kj, vj)
+            if fused:
+                out = empty_out((B, hq, d), True)
+                slots, ev = cache.append_decode_attn(layer, 0, B, kj, vj, qj[:, 0], out)
+            else:
+                slots, ev = cache.append_kv(layer, 0, B, chunk, kj, vj)
             for b in host:
                 led = ora.ledger(layer, b)
                 exp_slots = [(led.next_slot - chunk + j) % w for j in range(chunk)]
                 assert list(slots[b]) == exp_slots
-            if chunk == 1:
+            if fused:
+                pass
+            elif chunk == 1:
                 out = empty_out((B, hq, d), True)
                 cache.decode_attn(layer, 0, B, qj[:, 0], out)
             else:
@@ -181,9 +187,11 @@ def _full_size(wl, sampled_layers, sampled_streams, n_steps, chunk):
     cache.close()
 
 
-def test_qwen3b_batch64_full_size():
+@pytest.mark.parametrize("fused", [True, False])
+def test_qwen3b_batch64_full_size(fused):
+    """The benchmark's launch configuration (fused append + decode by default)."""
     wl = W_["qwen3b_batch64"]
-    _full_size(wl, [0, 17, 35], [0, 13, 63], 3, 1)
+    _full_size(wl, [0, 17, 35], [0, 13, 63], 3, 1, fused)
 
 
 def test_qwen3b_chunk8_full_size():
