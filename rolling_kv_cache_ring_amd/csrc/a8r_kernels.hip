@@ -371,7 +371,7 @@ __device__ __forceinline__ void load_coef(const float2* table, int row, int gq, 
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) cf[kk][j] = p[8 * kk + j];
+        for (int j = 0; j < 4; ++j) cf[kk][j] = p[16 * kk + j];   // pairs 32*kk + 2j, 2j + 1
 }
 
 // Rotates a lane's slice of a bf16 row (dims 8*gq + 32*kk + e) by the pairs in
