@@ -32,6 +32,7 @@ constexpr int kMaxSplits = 16;     // most key splits per (stream, KV head)
 constexpr int kMaxPartialQ = 16;   // chunk sizes above this run without splits
 constexpr size_t kAlign = 256;
 constexpr int kBatch = 128;        // streams per launch (their state travels in the arguments)
+constexpr int kMaxRowGroups = 4;   // query row groups of one KV head in the chunk kernel
 
 struct DevState {
     int64_t next_pos;   // absolute position of the next token
@@ -56,7 +57,7 @@ struct Geometry {
     DevState* state;
     float* part_o;      // split partials: [n_streams][n_kv_heads][kMaxSplits][rows_max][D]
     float* part_ml;     // [n_streams][n_kv_heads][kMaxSplits][rows_max][2]
-    int* counters;      // [n_streams][n_kv_heads] split arrival counters, 0 between calls
+    int* counters;      // [n_streams][n_kv_heads][kMaxRowGroups] split arrival counters, 0 between calls
     int n_layers, n_streams, hq, hkv, group, d, window, w_pad;
     int elem_bytes;     // 2 (bf16) or 4 (f32)
     int rows_max;       // max(1, min(max_chunk, kMaxPartialQ)) * group

@@ -673,7 +673,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     // block in; the last block of the pair merges every split's partials
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int* counter = &g.counters[bi * g.hkv + kh];
+    int* counter = &g.counters[(bi * g.hkv + kh) * kMaxRowGroups];
     if (tid == 0) {
         const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == n_split - 1);
@@ -695,6 +695,341 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             num += f * __hip_atomic_load(&g.part_o[pr * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         out[((int64_t)bi * g.hq + kh * G + h) * D + d] = f32_to_bf16_bits(num / den);
+    }
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------- MFMA chunk ----
+// bf16 attention for C new positions per stream (several per audio clock) in
+// one block per (stream, KV head, split): the C x G query rows of a KV head
+// (row = c*G + hg) form NQ column blocks of 16, so QK^T and PV are real
+// contractions on v_mfma_f32_16x16x32_bf16 (64 rows for 8 positions x 8 heads).
+//
+// Same ring walk, LDS staging and split merge as decode_mfma.  The rotation is
+// split differently: each query row is rotated once, by its own re-based index
+// r_q(c) = L - C + c; each key row is rotated by R(rho + t), composed per
+// visit from R(rho) (a table row fetched with the visit) and R(t) (t < 32,
+// staged in LDS):  (c, s)(a + b) = (c_a c_b - s_a s_b, s_a c_b + c_a s_b).
+// Query c sees keys with index <= r_q(c): causal inside the chunk, the whole
+// older window before it.  The first visit (rho = -t_o, and rho + W for the
+// window's newest keys sharing the oldest key's tile) reads its key rotations
+// straight from the table rows of the keys' indices.
+template <int D>
+__device__ __forceinline__ void compose(const float4 (&a)[D / 64][4], const float2* __restrict__ bt,
+                                        float4 (&out)[D / 64][4]) {
+    // bt: this lane's R(t) pairs in LDS (dims 8*gq + 32*kk + e), as float2
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 x = a[kk][j];
+            const float4 y = *(const float4*)(bt + 32 * kk + 2 * j);
+            out[kk][j] = float4{x.x * y.x - x.y * y.y, x.y * y.x + x.x * y.y,
+                                x.z * y.z - x.w * y.w, x.w * y.z + x.z * y.w};
+        }
+}
+
+template <int D, int NQ>
+__global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, StreamBatch st, int C,
+                                                     const uint16_t* __restrict__ q,
+                                                     uint16_t* __restrict__ out, int n_split) {
+    // NQ column blocks of 16 query rows per block; row group rg covers rows
+    // 16*NQ*rg .. 16*NQ*(rg+1)-1 (blockIdx.x = rg * n_split + split)
+    constexpr int KK = D / 32, NB = D / 16, NP = D / 2, HP = D / 64;
+    constexpr int kBuf = DecodeLds<D>::kBytes;
+    constexpr int kLoadsPerVisit = DecodeLds<D>::kChunks + 4 * HP;
+    constexpr int kRows = 16 * NQ;
+    // LDS: per wave two visit buffers (two distinct objects), the rotated query
+    // rows in MFMA B-operand order (shared by the 4 waves), R(t) for t < 32.
+    // After the walk the visit buffers hold the cross-wave merge and the query
+    // area holds the per-row (m, l) values.
+    __shared__ __align__(16) unsigned char lds_tiles_a[4 * kBuf];
+    __shared__ __align__(16) unsigned char lds_tiles_b[4 * kBuf];
+    __shared__ __align__(16) unsigned char q_lds[NQ * KK * 1024];
+    __shared__ __align__(16) float2 rt_lds[kTile * NP];
+    static_assert(4 * kRows * D * 4 <= 8 * kBuf, "merge buffer does not fit");
+    static_assert(4 * kRows * 2 * 4 + 16 <= NQ * KK * 1024, "(m, l) buffer does not fit");
+    float (*red_o)[kRows][D] = (float (*)[kRows][D])lds_tiles_a;   // spans both tile arrays
+    float (*red_ml)[kRows][2] = (float (*)[kRows][2])q_lds;
+    int* s_last = (int*)(q_lds + 4 * kRows * 2 * 4);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+    const int bi = blockIdx.z, kh = blockIdx.y;
+    const int rg = blockIdx.x / n_split, split = blockIdx.x - rg * n_split;
+    const int b = st.b0 + bi, G = g.group, W = g.window;
+    const int rows = C * G;                       // query rows of this KV head
+    const int row0 = rg * kRows;                  // first row of this block
+    const int n_rows = min(kRows, rows - row0);   // rows this block handles
+    unsigned char* buf_a = lds_tiles_a + wave * kBuf;
+    unsigned char* buf_b = lds_tiles_b + wave * kBuf;
+
+    DecodeCtx c;
+    const int L = st.length[bi];
+    c.L = L;
+    c.W = W;
+    c.oldest = st.next_slot[bi] - L < 0 ? st.next_slot[bi] - L + W : st.next_slot[bi] - L;
+    c.rq = L - C;                      // index of the chunk's first query
+    c.n_tiles = g.w_pad / kTile;
+    c.p0t = c.oldest / kTile;
+    c.t_o = c.oldest - c.p0t * kTile;
+    c.tb0 = 8 * (n >> 2) + (n & 3);
+    c.tb1 = c.tb0 + 4;
+    c.gq = gq;
+    c.n = n;
+    c.scale_log2 = g.scale_log2;
+    c.table = g.table;
+    const int64_t pair = pair_index(g, layer, b, kh);
+    c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
+    c.vp = (const uint16_t*)g.v_ring + pair * g.w_pad * D;
+    int n_visit;
+    {
+        int last = c.oldest + L - 1;
+        if (last < W) {
+            n_visit = last / kTile - c.p0t + 1;
+        } else {
+            last -= W;
+            n_visit = c.n_tiles - c.p0t + last / kTile + 1;
+            if (n_visit > c.n_tiles) n_visit = c.n_tiles;
+        }
+    }
+    const int per = (n_visit + n_split - 1) / n_split;
+    const int k0 = split * per, k1 = min(n_visit, k0 + per);
+
+    // Issues a visit's loads: K/V into the LDS buffer, R(rho) into registers
+    // (visits after the first; rho >= 0 there).
+    auto issue = [&](int kv, unsigned char* buf, DecodeCoef<D>& t) {
+        const int p = visit_tile(c, kv);
+        const int s0 = p * kTile;
+        const uint16_t* r0 = c.kp + (int64_t)(s0 + c.tb0) * D + 8 * gq;
+        const uint16_t* r1 = c.kp + (int64_t)(s0 + c.tb1) * D + 8 * gq;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            __builtin_amdgcn_global_load_lds((const void*)(r0 + 32 * kk), (lds_void*)(buf + kk * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(r1 + 32 * kk), (lds_void*)(buf + (KK + kk) * 1024), 16,
+                                             0, 0);
+        }
+        const uint16_t* vb = c.vp + ((int64_t)(p * 4 + gq) * D + n) * 8;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)nb * 16 * 8),
+                                             (lds_void*)(buf + (2 * KK + nb) * 1024), 16, 0, 0);
+        load_coef<D>(c.table, kv == 0 ? 0 : visit_rho(c, kv, s0), gq, t.qc);
+    };
+    DecodeCoef<D> ca, cb;
+    int k = k0 + wave;
+    if (k < k1) issue(k, buf_a, ca);
+
+    for (int idx = tid; idx < kTile * NP; idx += 256) rt_lds[idx] = g.table[idx];
+    // wave w rotates query column block w (rows 16w .. 16w+15 of the block) by
+    // R(L - C + c) and stores it in B-operand order
+    if (wave < NQ) {
+        const int row = row0 + 16 * wave + n;
+        bf16x8 qb[KK];
+        if (row < rows) {
+            const int cc = row / G, h = kh * G + (row - cc * G);
+            const uint16_t* qp = q + (((int64_t)bi * C + cc) * g.hq + h) * D + 8 * gq;
+            u32x4 qr[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) qr[kk] = *(const u32x4*)(qp + 32 * kk);
+            float4 cq4[HP][4];
+            load_coef<D>(g.table, c.rq + cc, gq, cq4);
+            rotate_row<D>(cq4, qr, qb);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qb[kk][e] = (__bf16)0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            *((bf16x8*)(q_lds + (wave * KK + kk) * 1024) + lane) = qb[kk];
+    }
+    // each column's query index for the causal mask (-1: padding row)
+    int rq_col[NQ];
+#pragma unroll
+    for (int cq = 0; cq < NQ; ++cq) {
+        const int row = row0 + 16 * cq + n;
+        rq_col[cq] = row < rows ? c.rq + row / G : -1;
+    }
+    __syncthreads();   // rt_lds and q_lds ready
+
+    floatx4 o[NQ][NB];
+#pragma unroll
+    for (int cq = 0; cq < NQ; ++cq)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) o[cq][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m[NQ], l[NQ];
+#pragma unroll
+    for (int cq = 0; cq < NQ; ++cq) {
+        m[cq] = kNegBig;
+        l[cq] = 0.f;
+    }
+    const int r_last = L - 1;   // the newest query's index
+
+    auto compute = [&](int kv, const unsigned char* buf, const DecodeCoef<D>& t) {
+        const int p = visit_tile(c, kv);
+        const int s0 = p * kTile;
+        const int rho = visit_rho(c, kv, s0);
+        const bool seam = (kv == 0) && (c.t_o > 0);
+        const u32x4* lb = (const u32x4*)buf + lane;
+        bf16x8 kb[2][KK];
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int tt = bb ? c.tb1 : c.tb0;
+            float4 cf[HP][4];
+            if (kv == 0) {
+                // key index r = tt - t_o, or tt - t_o + W before the oldest slot
+                int r = tt - c.t_o;
+                if (seam && tt < c.t_o) r += W;
+                load_coef<D>(c.table, r < 0 ? 0 : r, gq, cf);
+            } else {
+                compose<D>(t.qc, rt_lds + tt * NP + 8 * gq, cf);
+            }
+            u32x4 kr[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) kr[kk] = lb[(bb * KK + kk) * 64];
+            rotate_row<D>(cf, kr, kb[bb]);
+        }
+        const bool full = (kv != 0) && (rho + kTile <= c.rq + 1) && (s0 + kTile <= W);
+        const bf16x8* qlb = (const bf16x8*)q_lds + lane;
+#pragma unroll
+        for (int cq = 0; cq < NQ; ++cq) {
+            floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const bf16x8 qv = qlb[(cq * KK + kk) * 64];
+                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[0][kk], qv, a0, 0, 0, 0);
+                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[1][kk], qv, a1, 0, 0, 0);
+            }
+            float s[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] *= c.scale_log2;
+            if (!full) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tt = 8 * gq + e;
+                    int r = rho + tt;
+                    if (seam && tt < c.t_o) r += W;
+                    const bool ok = (r >= 0) && (r <= r_last) && (rq_col[cq] < 0 || r <= rq_col[cq]) &&
+                                    (s0 + tt < W);
+                    if (!ok) s[e] = -INFINITY;
+                }
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (mx > m[cq] + 8.f) {
+                const float alpha = exp2f(m[cq] - mx);
+                l[cq] *= alpha;
+#pragma unroll
+                for (int i = 0; i < NB; ++i) o[cq][i] *= alpha;
+                m[cq] = mx;
+            }
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe = exp2f(s[e] - m[cq]);
+                l[cq] += pe;
+                pb[e] = (__bf16)pe;
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const u32x4 vv = lb[(2 * KK + nb) * 64];
+                o[cq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[cq][nb],
+                                                                    0, 0, 0);
+            }
+        }
+    };
+
+    while (k < k1) {
+        int kn = k + 4;
+        issue(kn < k1 ? kn : k, buf_b, cb);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerVisit));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(k, buf_a, ca);
+        k = kn;
+        if (k >= k1) break;
+        kn = k + 4;
+        issue(kn < k1 ? kn : k, buf_a, ca);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerVisit));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(k, buf_b, cb);
+        k = kn;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+#pragma unroll
+    for (int cq = 0; cq < NQ; ++cq) {
+        l[cq] += __shfl_xor(l[cq], 16);
+        l[cq] += __shfl_xor(l[cq], 32);
+    }
+    __syncthreads();   // every wave is done with its visit buffers and the query rows
+#pragma unroll
+    for (int cq = 0; cq < NQ; ++cq) {
+        const int lr = 16 * cq + n;
+        if (gq == 0) {
+            red_ml[wave][lr][0] = m[cq];
+            red_ml[wave][lr][1] = l[cq];
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) red_o[wave][lr][16 * nb + 4 * gq + j] = o[cq][nb][j];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < n_rows * D; idx += 256) {
+        const int lr = idx / D, d = idx - lr * D, row = row0 + lr;
+        float mm = red_ml[0][lr][0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) mm = fmaxf(mm, red_ml[w][lr][0]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float f = exp2f(red_ml[w][lr][0] - mm);
+            num += f * red_o[w][lr][d];
+            den += f * red_ml[w][lr][1];
+        }
+        const int cc = row / G, h = kh * G + (row - cc * G);
+        if (n_split == 1) {
+            out[(((int64_t)bi * C + cc) * g.hq + h) * D + d] = f32_to_bf16_bits(num / den);
+        } else {
+            const int64_t pr = part_row(g, bi, kh, split, row);
+            __hip_atomic_store(&g.part_o[pr * D + d], num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == 0) {
+                __hip_atomic_store(&g.part_ml[pr * 2], mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&g.part_ml[pr * 2 + 1], den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    if (n_split == 1) return;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int* counter = &g.counters[(bi * g.hkv + kh) * kMaxRowGroups + rg];
+    if (tid == 0) {
+        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_last = (prev == n_split - 1);
+    }
+    __syncthreads();
+    if (!*s_last) return;
+    for (int idx = tid; idx < n_rows * D; idx += 256) {
+        const int row = row0 + idx / D, d = idx % D;
+        float mm = kNegBig;
+        for (int sp = 0; sp < n_split; ++sp)
+            mm = fmaxf(mm, __hip_atomic_load(&g.part_ml[part_row(g, bi, kh, sp, row) * 2], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+        float num = 0.f, den = 0.f;
+        for (int sp = 0; sp < n_split; ++sp) {
+            const int64_t pr = part_row(g, bi, kh, sp, row);
+            const float f =
+                exp2f(__hip_atomic_load(&g.part_ml[pr * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - mm);
+            den += f * __hip_atomic_load(&g.part_ml[pr * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            num += f * __hip_atomic_load(&g.part_o[pr * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const int cc = row / G, h = kh * G + (row - cc * G);
+        out[(((int64_t)bi * C + cc) * g.hq + h) * D + d] = f32_to_bf16_bits(num / den);
     }
     if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -749,6 +1084,30 @@ hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, 
     return hipGetLastError();
 }
 
+template <int D, int NQ>
+hipError_t run_chunk_mfma(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q, void* out,
+                          int n_cu, hipStream_t s) {
+    const int n_rg = (n_q * g.group + 16 * NQ - 1) / (16 * NQ);
+    const int n_split = pick_splits(st.nb * g.hkv * n_rg, g.w_pad / kTile, n_cu, 4);
+    hipLaunchKernelGGL((chunk_mfma<D, NQ>), dim3(n_split * n_rg, g.hkv, st.nb), dim3(256), 0, s, g, layer, st,
+                       n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
+    return hipGetLastError();
+}
+
+// At most two 16-row column blocks per block keep the accumulators and the
+// per-row softmax state in registers; larger chunks use several row groups.
+template <int D>
+hipError_t run_chunk_mfma_nq(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q,
+                             void* out, int n_cu, hipStream_t s) {
+    return n_q * g.group <= 16 ? run_chunk_mfma<D, 1>(g, layer, st, n_q, q, out, n_cu, s)
+                               : run_chunk_mfma<D, 2>(g, layer, st, n_q, q, out, n_cu, s);
+}
+
+bool mfma_chunk_ok(const Geometry& g, int n_q) {
+    return g.elem_bytes == 2 && (g.d == 64 || g.d == 128) && n_q >= 2 && n_q <= kMaxPartialQ &&
+           n_q * g.group <= 32 * kMaxRowGroups;
+}
+
 }  // namespace
 
 // ================================================================ launchers ==
@@ -774,6 +1133,9 @@ hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now
     if (allow_mfma && n_q == 1 && mfma_decode_ok(g))
         return g.d == 128 ? run_decode_mfma<128>(g, layer, now, q, out, n_cu, nullptr, nullptr, s)
                           : run_decode_mfma<64>(g, layer, now, q, out, n_cu, nullptr, nullptr, s);
+    if (allow_mfma && mfma_chunk_ok(g, n_q))
+        return g.d == 128 ? run_chunk_mfma_nq<128>(g, layer, now, n_q, q, out, n_cu, s)
+                          : run_chunk_mfma_nq<64>(g, layer, now, n_q, q, out, n_cu, s);
     int sp = 1;
     if (n_q <= kMaxPartialQ) {
         const int n_rg = (n_q * g.group + 63) / 64;
