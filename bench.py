@@ -47,7 +47,100 @@ def parse():
                          "a8r_append_kv + a8r_decode_attn (separate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB device copy 5 times (counter calibration)")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="summarize rocprofv3 CSV output under DIR (no GPU work); see profiles/")
+    ap.add_argument("--summary-command", default="", help="command line recorded in the summary")
     return ap.parse_args()
+
+
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe(torch):
+    """A plain device copy of known size: 1 GiB read + 1 GiB written per launch."""
+    src = torch.empty(COPY_PROBE_BYTES // 2, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def summarize(args):
+    """Reads rocprofv3 CSVs (kernel_stats / counter_collection) under a directory
+    and prints a markdown summary; for counter runs also updates
+    profiles/pmc_traffic.json with the calibrated HBM bytes per attention launch."""
+    import csv
+    import glob
+    from collections import defaultdict
+    d = args.summarize
+    lines = [f"command: `{args.summary_command}`", ""]
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    for f in stats:
+        rows = list(csv.DictReader(open(f)))
+        lines.append("| kernel | calls | avg us | min us | max us | share |")
+        lines.append("|---|---|---|---|---|---|")
+        for r in rows:
+            name = r["Name"]
+            short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            lines.append(f"| `{short[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.1f}% |")
+    cc = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if cc:
+        per = defaultdict(lambda: defaultdict(float))
+        calls = defaultdict(set)
+        rows_all = []
+        for f in cc:
+            rows_all += list(csv.DictReader(open(f)))
+        is_attn = lambda n: "decode_mfma" in n or "chunk_mfma" in n
+        last_attn = max([int(r["Dispatch_Id"]) for r in rows_all if is_attn(r["Kernel_Name"])] + [0])
+        for r in rows_all:
+            name = r["Kernel_Name"]
+            if is_attn(name):
+                key = "attention"
+            elif "copy" in name.lower() and int(r["Dispatch_Id"]) > last_attn:
+                key = "copy"        # the calibration copies run after the last attention launch
+            else:
+                continue
+            per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            calls[key].add(r["Dispatch_Id"])
+        lines.append("| kernel | dispatches | counter | KiB per dispatch |")
+        lines.append("|---|---|---|---|")
+        avg = {}
+        for key, cnt in per.items():
+            for cname, v in cnt.items():
+                a = v / max(1, len(calls[key]))
+                avg[(key, cname)] = a
+                lines.append(f"| {key} | {len(calls[key])} | {cname} | {a:.1f} |")
+        rec_path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+        try:
+            rec = json.load(open(rec_path))
+        except (OSError, ValueError):
+            rec = {}
+        wl = args.workload
+        entry = rec.get(wl, {})
+        if entry.get("kernel_sha256_16") != kernel_hash():
+            entry = {}      # counters taken on an older kernel source no longer apply
+        for cname, copy_bytes in (("FETCH_SIZE", COPY_PROBE_BYTES), ("WRITE_SIZE", COPY_PROBE_BYTES)):
+            if ("copy", cname) in avg and ("attention", cname) in avg:
+                factor = copy_bytes / (avg[("copy", cname)] * 1024)
+                entry[cname.lower() + "_factor"] = factor
+                entry[cname.lower() + "_bytes"] = avg[("attention", cname)] * 1024 * factor
+                lines.append(f"\n{cname}: copy probe counts {avg[('copy', cname)]:.0f} KiB for "
+                             f"{copy_bytes / 1024:.0f} KiB moved -> scale factor {factor:.4f}; attention kernel "
+                             f"{avg[('attention', cname)] * 1024 * factor / 1e6:.2f} MB per launch")
+        entry["kernel_sha256_16"] = kernel_hash()
+        entry["path"] = args.path
+        if "fetch_size_bytes" in entry and "write_size_bytes" in entry:
+            entry["bytes_per_launch"] = round(entry["fetch_size_bytes"] + entry["write_size_bytes"])
+            lines.append(f"\nrecorded {rec_path}: {entry['bytes_per_launch'] / 1e6:.2f} MB per launch")
+        rec[wl] = entry
+        os.makedirs(os.path.dirname(rec_path), exist_ok=True)
+        json.dump(rec, open(rec_path, "w"), indent=1, sort_keys=True)
+    print("\n".join(lines))
 
 
 def algorithmic_bytes(wl, live):
@@ -125,6 +218,9 @@ def cpu_baseline(wl, seconds):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               "(streams shard across GPUs with no exchange; see DESIGN.md). Run with --gpus 1.",
@@ -179,26 +275,30 @@ def main():
 
     fused = c == 1 and args.path == "fused"
 
-    def step(i, timers=None):
+    def check(st):
+        if st:
+            raise a8r.A8RError(st, L.a8r_last_error().decode())
+
+    def step(i):
         kp, vp, qp = k_ptrs[i % POOL], v_ptrs[i % POOL], q_ptrs[i % POOL]
         for layer in range(NL):
             if fused:
-                if timers is not None:
-                    timers[layer][0].record(stream)
-                st = L.a8r_append_decode_attn(h, layer, 0, B, kp[layer], vp[layer], qp[layer], o_ptrs[layer],
-                                              None, None)
+                check(L.a8r_append_decode_attn(h, layer, 0, B, kp[layer], vp[layer], qp[layer],
+                                               o_ptrs[layer], None, None))
+                continue
+            check(L.a8r_append_kv(h, layer, 0, B, c, kp[layer], vp[layer], None, None))
+            if c == 1:
+                check(L.a8r_decode_attn(h, layer, 0, B, qp[layer], o_ptrs[layer]))
             else:
-                st = L.a8r_append_kv(h, layer, 0, B, c, kp[layer], vp[layer], None, None)
-                if timers is not None:
-                    timers[layer][0].record(stream)
-                if c == 1:
-                    st |= L.a8r_decode_attn(h, layer, 0, B, qp[layer], o_ptrs[layer])
-                else:
-                    st |= L.a8r_chunk_attn(h, layer, 0, B, c, qp[layer], o_ptrs[layer])
-            if timers is not None:
-                timers[layer][1].record(stream)
-            if st:
-                raise a8r.A8RError(st, L.a8r_last_error().decode())
+                check(L.a8r_chunk_attn(h, layer, 0, B, c, qp[layer], o_ptrs[layer]))
+
+    def attention_only(i):
+        qp = q_ptrs[i % POOL]
+        for layer in range(NL):
+            if c == 1:
+                check(L.a8r_decode_attn(h, layer, 0, B, qp[layer], o_ptrs[layer]))
+            else:
+                check(L.a8r_chunk_attn(h, layer, 0, B, c, qp[layer], o_ptrs[layer]))
 
     for i in range(args.warmup):
         step(i)
@@ -216,16 +316,25 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
     steps_per_s = 1000.0 / ms
 
-    # per-launch duration of the attention kernel(s): events around every
-    # attention call of a second pass over the same number of steps
-    n_t = min(args.steps, 200)
-    timers = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(NL)] for _ in range(n_t)]
-    for i in range(n_t):
-        step(i, [[a, b] for a, b in timers[i]])
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for row in timers for a, b in row]
-    attn_ms = float(np.mean(durs))
+    # average launch duration of the attention kernel.  Fused path: the timed
+    # region launches nothing else (one kernel per layer), so it is the region
+    # time over its launches.  Separate path: a second pass launches only the
+    # attention calls (they leave the cache unchanged) back to back on the same
+    # stream, bracketed by one event pair.
+    if fused:
+        n_launch = args.steps * NL
+        attn_ms = ev0.elapsed_time(ev1) / n_launch
+    else:
+        n_t = min(args.steps, 200)
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for i in range(n_t):
+            attention_only(i)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        n_launch = n_t * NL
+        attn_ms = a0.elapsed_time(a1) / n_launch
 
     live = w  # every stream holds a full window after pre-fill
     bytes_launch = algorithmic_bytes(wl, live)
@@ -234,6 +343,9 @@ def main():
     achieved = bytes_launch / (attn_ms * 1e-3) / 1e9
     flops_launch = attention_flops(wl, live)
     traffic = traffic_from_profiles(args.workload)
+
+    if args.copy_probe:
+        copy_probe(torch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -269,6 +381,7 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": bytes_launch,
             "avg_launch_ms": round(attn_ms, 5),
+            "launches_timed": n_launch,
             "mfma_tflops": round(flops_launch / (attn_ms * 1e-3) / 1e12, 2),
             "mfma_frac_bf16_dense": round(flops_launch / (attn_ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
         },
