@@ -304,11 +304,13 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 // Rotation: with R(x) the split-half rotation by index x, the score is
 // <R(r_q) q, R(rho + t) k> = <R(r_q - rho) q, R(t) k> because rotations in each
 // 2-D plane compose additively and are orthogonal.  Each lane always handles
-// the same two key offsets t of a tile, so its R(t) coefficients are loaded
-// once and kept in registers; the query is rotated once per visit by
-// R(r_q - rho) (a table row < W + 32) whose coefficients are fetched together
-// with the visit's K/V.  Every coefficient comes from the float64-built table;
-// no absolute position enters float arithmetic.
+// the same two key offsets t of a tile, so its R(t) coefficients stay in
+// registers for the whole walk; the query is rotated once per visit by
+// R(r_q - rho), a table row (< W + 32) fetched with the visit's keys.  On the
+// first visit the newest keys (offsets before the oldest slot) use
+// R(t + W) = R(W) R(t), composed in float32 from the R(W) row.  Every
+// coefficient comes from the float64-built table; no absolute position enters
+// float arithmetic.
 //
 // MFMA mapping (v_mfma_f32_16x16x32_bf16, lane l = 16*gq + n):
 //   QK: S^T[key][head] = K_rot[key][dims] * Q_rot^T; A row n of tile half b is
@@ -316,23 +318,31 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 //       keys 8*gq .. 8*gq+7 for head n -- exactly the B operand of PV.
 //   PV: O^T[d][head] = V^T[d][keys] * P^T; the A operand is 8 consecutive slots
 //       of one dim, i.e. 16 bytes of the transposed 8-slot V block.
-// Query heads beyond the group (n >= G) are zero rows and are discarded.
+// Columns n >= G (padding) carry a copy of head 0 and are discarded.
 //
-// Each wave keeps the next visit's loads in flight while it computes the
-// current one (two register buffers).  The splits of one (stream, KV head)
-// publish {m, l, O} partials with agent-coherent stores; the last block to
-// arrive (agent-scope atomic counter) merges them and re-arms the counter.
+// Memory pipeline: every global read of the kernel is a direct global->LDS
+// load (global_load_lds_dwordx4, 16 bytes per lane at LDS base + 16*lane), so
+// data in flight holds no registers.  Each wave owns two visit buffers, each
+// split in a K part (32 rows, whole cache lines per instruction, XOR-swizzled
+// for conflict-free MFMA operand reads, plus the visit's query-rotation row)
+// and a V part.  Order of issue: K(k), V(k), K(k+4), V(k+4); the scores of
+// visit k wait only for K(k), its PV only for V(k), and each part is refilled
+// with the visit two ahead as soon as it has been read, so about three
+// quarters of the wave's LDS are in flight at any time.  The waits are explicit
+// vmcnt counts; the DMA destinations are hidden from the compiler's own wait
+// insertion (see opaque_lds), which would otherwise drain the queue.
+//
+// The splits of one (stream, KV head) publish {m, l, O} partials with
+// agent-coherent stores; the last block to arrive (agent-scope atomic counter)
+// merges them and re-arms the counter.
 //
 // Fused append: with k_new != nullptr the state in the arguments is the state
 // before the append, the window is the one after it, and the wave that owns
 // the new token's tile writes the token into its ring slot before it reads that
 // tile (no other wave touches that slot).
 
-// One wave's share of a visit, staged in LDS by direct global->LDS loads
-// (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16*l), so data in
-// flight holds no VGPRs.  Layout of one buffer: 2*(D/32) 1-KiB K chunks
-// (tile half b, dim chunk kk) then D/16 1-KiB V chunks; each lane reads back
-// exactly the 16 bytes it requested.
+// Used by the chunk kernel: one buffer holds a visit's K rows (2*(D/32) 1-KiB
+// chunks, lane l's 16 bytes at 16*l) and V blocks (D/16 chunks).
 template <int D>
 struct DecodeLds {
     static constexpr int kChunks = 2 * (D / 32) + D / 16;
@@ -374,6 +384,16 @@ __device__ __forceinline__ void load_coef(const float2* table, int row, int gq, 
         for (int j = 0; j < 4; ++j) cf[kk][j] = p[16 * kk + j];   // pairs 32*kk + 2j, 2j + 1
 }
 
+// The same pairs read from a table row staged in LDS.
+template <int D>
+__device__ __forceinline__ void lds_coef(const unsigned char* row, int gq, float4 (&cf)[D / 64][4]) {
+    const float4* p = (const float4*)row + 4 * gq;
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cf[kk][j] = p[16 * kk + j];
+}
+
 // Rotates a lane's slice of a bf16 row (dims 8*gq + 32*kk + e) by the pairs in
 // cf: x_i, x_{i+D/2} -> x_i c - x_{i+D/2} s, x_{i+D/2} c + x_i s, rounded to bf16.
 template <int D>
@@ -397,56 +417,142 @@ __device__ __forceinline__ void rotate_row(const float4 (&cf)[D / 64][4], const 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Issues every global load of a visit: K rows and V blocks into the wave's LDS
-// buffer `buf` (wave-uniform), the query rotation coefficients into registers.
+// The LDS destination of a direct global->LDS load, passed through an empty asm
+// so that the compiler cannot tie it to an LDS object: its own wait insertion
+// then leaves such loads alone (it would otherwise wait for every outstanding
+// load before LDS reads it cannot disambiguate).  Every read of DMA-written
+// data is preceded by an explicit vmcnt wait and lds_fence(), and a buffer is
+// refilled only after lgkmcnt(0), i.e. after the wave's reads of it are done.
+__device__ __forceinline__ lds_void* opaque_lds(unsigned char* p) {
+    // wave-uniform by construction; readfirstlane tells the compiler so
+    unsigned off = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void*)p);
+    asm volatile("" : "+s"(off));
+    return (lds_void*)(size_t)off;
+}
+
+// Compiler-level memory barrier (no instruction): loads and stores do not move
+// across it.
+__device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, opaque_lds(lds_dst), 16, 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8): "at most n vector-memory operations outstanding", and
+// "no LDS operation outstanding".
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// K part of a visit buffer: chunk (row r, 16-byte column col) of the 32 x D
+// tile at chunk position (D/8) r + 8 (col / 8) + ((col % 8) ^ swz(r)).  Each
+// DMA instruction then reads 64 / (D/8) consecutive rows (whole cache lines),
+// and the MFMA operand reads of eight consecutive lanes (rows tb(n)) fall on
+// distinct banks.  The visit's query-rotation row follows the 32 rows.
+__device__ __forceinline__ int k_swz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+
 template <int D>
-__device__ __forceinline__ void load_visit(const DecodeCtx& c, int k, unsigned char* buf, DecodeCoef<D>& t) {
-    constexpr int KK = D / 32, NB = D / 16;
-    const int p = visit_tile(c, k);
-    const int s0 = p * kTile;
-    const uint16_t* r0 = c.kp + (int64_t)(s0 + c.tb0) * D + 8 * c.gq;
-    const uint16_t* r1 = c.kp + (int64_t)(s0 + c.tb1) * D + 8 * c.gq;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        __builtin_amdgcn_global_load_lds((const void*)(r0 + 32 * kk), (lds_void*)(buf + kk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(r1 + 32 * kk), (lds_void*)(buf + (KK + kk) * 1024), 16, 0,
-                                         0);
-    }
-    const uint16_t* vb = c.vp + ((int64_t)(p * 4 + c.gq) * D + c.n) * 8;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)nb * 16 * 8),
-                                         (lds_void*)(buf + (2 * KK + nb) * 1024), 16, 0, 0);
-    load_coef<D>(c.table, c.rq - visit_rho(c, k, s0), c.gq, t.qc);
+__device__ __forceinline__ int k_pos(int r, int col) {
+    return (D / 8) * r + 8 * (col >> 3) + ((col & 7) ^ k_swz(r));
 }
 
 template <int D>
-__device__ __forceinline__ void compute_visit(const DecodeCtx& c, int k, const unsigned char* buf,
-                                              const DecodeCoef<D>& t, const u32x4 (&qraw)[D / 32],
-                                              const float4 (&cf0)[D / 64][4], const float4 (&cf1)[D / 64][4],
-                                              floatx4 (&o)[D / 16], float& m, float& l, int lane) {
+struct DecBuf {
+    static constexpr int kK = 2 * (D / 32) * 1024 + 1024;   // K rows + rotation row
+    static constexpr int kV = (D / 16) * 1024;
+    static constexpr int nK = 2 * (D / 32) + 1;              // DMA instructions per part
+    static constexpr int nV = D / 16;
+};
+
+// Row `row` of the rotation table (D/2 float2 = 4D bytes) into LDS; lanes past
+// the row re-read its last 16 bytes.
+template <int D>
+__device__ __forceinline__ void dma_table_row(const float2* table, int row, int lane, unsigned char* dst) {
+    const int off = 16 * lane < 4 * D ? 16 * lane : 4 * D - 16;
+    dma16((const unsigned char*)(table + (int64_t)row * (D / 2)) + off, dst);
+}
+
+template <int D>
+__device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, unsigned char* kbuf) {
+    constexpr int RPI = 64 / (D / 8);            // rows per instruction
+    const int p = visit_tile(c, k);
+    const int s0 = p * kTile;
+    const int rl = lane / (D / 8), sl = lane % (D / 8);
+#pragma unroll
+    for (int j = 0; j < 2 * (D / 32); ++j) {
+        const int r = RPI * j + rl;
+        const int col = 8 * (sl >> 3) + ((sl & 7) ^ k_swz(r));
+        dma16(c.kp + (int64_t)(s0 + r) * D + 8 * col, kbuf + j * 1024);
+    }
+    dma_table_row<D>(c.table, c.rq - visit_rho(c, k, s0), lane, kbuf + 2 * (D / 32) * 1024);
+}
+
+template <int D>
+__device__ __forceinline__ void dec_load_v(const DecodeCtx& c, int k, unsigned char* vbuf) {
+    const int p = visit_tile(c, k);
+    const uint16_t* vb = c.vp + ((int64_t)(p * 4 + c.gq) * D + c.n) * 8;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) dma16(vb + (int64_t)nb * 16 * 8, vbuf + nb * 1024);
+}
+
+// Coefficients of R(t + W) = R(W) R(t) where `wrap` (the lane's key offset lies
+// before the oldest slot on the first visit), else R(t).
+template <int D>
+__device__ __forceinline__ void seam_coef(const float4 (&rw)[D / 64][4], const float4 (&cf)[D / 64][4], bool wrap,
+                                          float4 (&out)[D / 64][4]) {
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 a = cf[kk][j], w = rw[kk][j];
+            const float4 comp = {a.x * w.x - a.y * w.y, a.y * w.x + a.x * w.y,
+                                 a.z * w.z - a.w * w.w, a.w * w.z + a.z * w.w};
+            out[kk][j] = wrap ? comp : a;
+        }
+}
+
+// A visit's K part copied from LDS into registers: the query-rotation pairs
+// R(r_q - rho) and the lane's two K rows (tb0, tb1; dims 8*gq + 32*kk + e), so
+// that the buffer can be refilled before the arithmetic starts.
+template <int D>
+struct DecK {
+    float4 qc[D / 64][4];
+    u32x4 k0[D / 32], k1[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void dec_read_k(const DecodeCtx& c, const unsigned char* kbuf, DecK<D>& r) {
+    constexpr int KK = D / 32;
+    lds_coef<D>(kbuf + KK * 2048, c.gq, r.qc);
+    const u32x4* kt = (const u32x4*)kbuf;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        r.k0[kk] = kt[k_pos<D>(c.tb0, c.gq + 4 * kk)];
+        r.k1[kk] = kt[k_pos<D>(c.tb1, c.gq + 4 * kk)];
+    }
+}
+
+// Scores of visit k from its K part and the online-softmax update; returns
+// this lane's eight probabilities (keys 8*gq .. 8*gq+7, head n) as bf16.
+template <int D>
+__device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const DecK<D>& r,
+                                             const u32x4 (&qraw)[D / 32], const float4 (&cf0)[D / 64][4],
+                                             const float4 (&cf1)[D / 64][4], floatx4 (&o)[D / 16], float& m,
+                                             float& l) {
     constexpr int KK = D / 32, NB = D / 16;
     const int p = visit_tile(c, k);
     const int s0 = p * kTile;
     const int rho = visit_rho(c, k, s0);
-    const u32x4* lb = (const u32x4*)buf + lane;        // this lane's 16 bytes of each 1-KiB chunk
     bf16x8 qb[KK];
-    rotate_row<D>(t.qc, qraw, qb);            // query by R(r_q - rho)
-    // keys by R(t); on the first visit the caller has swapped in R(t + W) for the
-    // window's newest keys that share the oldest key's tile (index rho + t + W)
+    rotate_row<D>(r.qc, qraw, qb);            // query by R(r_q - rho)
     const bool seam = (k == 0) && (c.t_o > 0);
     floatx4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
     {
-        u32x4 kr[KK];
         bf16x8 kb[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kr[kk] = lb[kk * 64];
-        rotate_row<D>(cf0, kr, kb);
+        rotate_row<D>(cf0, r.k0, kb);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], sc0, 0, 0, 0);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kr[kk] = lb[(KK + kk) * 64];
-        rotate_row<D>(cf1, kr, kb);
+        rotate_row<D>(cf1, r.k1, kb);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], sc1, 0, 0, 0);
     }
@@ -458,9 +564,9 @@ __device__ __forceinline__ void compute_visit(const DecodeCtx& c, int k, const u
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int tt = 8 * c.gq + e;
-            int r = rho + tt;
-            if (seam && tt < c.t_o) r += c.W;
-            const bool ok = (r >= 0) && (r < c.L) && (s0 + tt < c.W);
+            int rr = rho + tt;
+            if (seam && tt < c.t_o) rr += c.W;
+            const bool ok = (rr >= 0) && (rr < c.L) && (s0 + tt < c.W);
             if (!ok) s[e] = -INFINITY;
         }
     }
@@ -484,16 +590,22 @@ __device__ __forceinline__ void compute_visit(const DecodeCtx& c, int k, const u
         l += pe;
         pb[e] = (__bf16)pe;
     }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 vv = lb[(2 * KK + nb) * 64];
-        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[nb], 0, 0, 0);
-    }
+    return pb;
 }
 
-// s_waitcnt immediate for "at most n vector-memory operations outstanding"
-// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+template <int D>
+__device__ __forceinline__ void dec_read_v(const unsigned char* vbuf, int lane, u32x4 (&v)[D / 16]) {
+    const u32x4* lb = (const u32x4*)vbuf + lane;       // each lane reads the 16 bytes it loaded
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) v[nb] = lb[nb * 64];
+}
+
+template <int D>
+__device__ __forceinline__ void dec_pv(const u32x4 (&v)[D / 16], bf16x8 pb, floatx4 (&o)[D / 16]) {
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb)
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[nb]), pb, o[nb], 0, 0, 0);
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, StreamBatch st,
@@ -502,25 +614,31 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
                                                       const uint16_t* __restrict__ k_new,
                                                       const uint16_t* __restrict__ v_new) {
     constexpr int KK = D / 32, NB = D / 16;
-    constexpr int kBuf = DecodeLds<D>::kBytes;
-    constexpr int kLoadsPerVisit = DecodeLds<D>::kChunks + 4 * (D / 64);
-    // per wave two visit buffers, as two distinct LDS objects so that the
-    // compiler can tell the buffer being read from the one being filled; after
-    // the walk the first one holds the cross-wave merge (4 x 16 x D floats)
-    __shared__ __align__(16) unsigned char lds_tiles_a[4 * kBuf];
-    __shared__ __align__(16) unsigned char lds_tiles_b[4 * kBuf];
+    using B = DecBuf<D>;
+    // per wave: buffer a and b, each a K part and a V part, four distinct LDS
+    // objects; then the block's R(t) rows (t < 32), query rows and R(W) row
+    __shared__ __align__(16) unsigned char lds_ka[4 * B::kK];
+    __shared__ __align__(16) unsigned char lds_va[4 * B::kV];
+    __shared__ __align__(16) unsigned char lds_kb[4 * B::kK];
+    __shared__ __align__(16) unsigned char lds_vb[4 * B::kV];
+    __shared__ __align__(16) unsigned char lds_rt[kTile * D * 4];
+    __shared__ __align__(16) unsigned char lds_q[4096];
+    __shared__ __align__(16) unsigned char lds_rw[1024];
     __shared__ float red_ml[4][16][2];
     __shared__ int s_last;
-    static_assert(4 * 16 * D * 4 <= 4 * kBuf, "merge buffer does not fit");
-    float (*red_o)[16][D] = (float (*)[16][D])lds_tiles_a;
+    static_assert(4 * 16 * D * 4 <= 4 * B::kK, "merge buffer does not fit");
+    float (*red_o)[16][D] = (float (*)[16][D])lds_ka;   // after the walk
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, gq = lane >> 4;
     const int bi = blockIdx.z, kh = blockIdx.y, split = blockIdx.x;
     const int b = st.b0 + bi, G = g.group, W = g.window;
     const bool fused = k_new != nullptr;
-    unsigned char* buf_a = lds_tiles_a + wave * kBuf;
-    unsigned char* buf_b = lds_tiles_b + wave * kBuf;
+    unsigned char* ka = lds_ka + wave * B::kK;
+    unsigned char* va = lds_va + wave * B::kV;
+    unsigned char* kb = lds_kb + wave * B::kK;
+    unsigned char* vb = lds_vb + wave * B::kV;
 
     // window after the (optional) append of one token
     const int s_prev = st.next_slot[bi];
@@ -566,67 +684,125 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             write_token<2>(g, pair, s_prev, lane, (const uint8_t*)k_new + src, (const uint8_t*)v_new + src);
         }
         __builtin_amdgcn_s_waitcnt(0);
-        if (kh == 0 && split == 0 && tid == 0) {
-            DevState ns;
-            ns.next_pos = st.next_pos[bi] + 1;
-            ns.length = L;
-            ns.next_slot = next_slot;
-            g.state[(int64_t)layer * g.n_streams + b] = ns;
-        }
     }
 
-    // the first visit's loads go out before anything else
-    DecodeCoef<D> ca, cb;
+    // Prologue, every load a direct global->LDS load (so the explicit wait
+    // counts are exact): a quarter of the R(t) rows, a quarter of the query
+    // block (clamped to it), the R(W) row (wave 0), ...
     int k = k0 + wave;
-    if (k < k1) load_visit<D>(c, k, buf_a, ca);
+    {
+        constexpr int kRt = kTile * D * 4 / 1024 / 4;     // R(t) instructions per wave
+#pragma unroll
+        for (int j = 0; j < kRt; ++j) {
+            const int off = (wave * kRt + j) * 1024;
+            dma16((const unsigned char*)g.table + off + 16 * lane, lds_rt + off);
+        }
+        const int qbytes = G * D * 2;
+        int qo = wave * 1024 + 16 * lane;
+        qo = qo < qbytes ? qo : qbytes - 16;
+        dma16((const unsigned char*)(q + ((int64_t)bi * g.hq + kh * G) * D) + qo, lds_q + wave * 1024);
+        if (wave == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
+    }
+    // then K(k), V(k), K(k + 4), V(k + 4) of the wave's first two visits (those
+    // that exist), and a wait for everything up to K(k)
+    if (k + 4 < k1) {
+        dec_load_k<D>(c, k, lane, ka);
+        dec_load_v<D>(c, k, va);
+        dec_load_k<D>(c, k + 4, lane, kb);
+        dec_load_v<D>(c, k + 4, vb);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV + B::nK + B::nV));
+    } else if (k < k1) {
+        dec_load_k<D>(c, k, lane, ka);
+        dec_load_v<D>(c, k, va);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
+    } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __builtin_amdgcn_s_barrier();                                    // ... and every other wave's
+    lds_fence();
 
     // the query stays as bf16 bits (the softmax scale is applied to the scores)
     u32x4 qraw[KK];
-    if (n < G) {
-        const uint16_t* qp = q + ((int64_t)bi * g.hq + kh * G + n) * D + 8 * gq;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qraw[kk] = *(const u32x4*)(qp + 32 * kk);
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qraw[kk] = u32x4{0u, 0u, 0u, 0u};
-    }
-    // R(t) of the lane's two key offsets, resident for the whole walk; the wave
-    // that starts with the seam visit uses R(t + W) for offsets before the oldest
-    // slot until that visit is done
-    const bool seam_first = (k == 0) && (k < k1) && (c.t_o > 0);
     float4 cf0[D / 64][4], cf1[D / 64][4];
-    load_coef<D>(g.table, seam_first && c.tb0 < c.t_o ? c.tb0 + W : c.tb0, gq, cf0);
-    load_coef<D>(g.table, seam_first && c.tb1 < c.t_o ? c.tb1 + W : c.tb1, gq, cf1);
+    {
+        const unsigned char* qrow = lds_q + (n < G ? n : 0) * D * 2 + 16 * gq;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qraw[kk] = *(const u32x4*)(qrow + 64 * kk);
+        lds_coef<D>(lds_rt + c.tb0 * D * 4, gq, cf0);
+        lds_coef<D>(lds_rt + c.tb1 * D * 4, gq, cf1);
+    }
 
     floatx4 o[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m = kNegBig, l = 0.f;
 
-    // Software pipeline over this wave's visits k0 + wave, +4, ...: the loads of
-    // the next visit are issued before the current one is computed.  Past the
-    // last visit the prefetch re-reads the current tile (a cache hit) into the
-    // other buffer, so the number of loads in flight is the same every time.
+    // Visits k0 + wave, +4, ... alternate between buffers a and b.  Per visit:
+    // wait for its K part, copy it to registers, refill the buffer with the
+    // visit two ahead (if there is one), compute the scores; then the same for
+    // the V part and PV.  The loads in flight after K(k) are V(k) and, if visit
+    // k + 4 exists, K(k + 4) and V(k + 4); after V(k) they are K(k + 4) and
+    // V(k + 4) and, if visit k + 8 exists, K(k + 8).  The wait counts follow
+    // (wave-uniform branches).
+    auto wait_k = [&](int kk) {
+        if (kk + 4 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV + B::nK + B::nV));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
+        __builtin_amdgcn_sched_barrier(0);
+        lds_fence();
+    };
+    auto wait_v = [&](int kk) {
+        if (kk + 8 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nK + B::nV + B::nK));
+        else if (kk + 4 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nK + B::nV));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_sched_barrier(0);
+        lds_fence();
+    };
     while (k < k1) {
-        int kn = k + 4;
-        load_visit<D>(c, kn < k1 ? kn : k, buf_b, cb);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerVisit));   // visit k has landed
-        __builtin_amdgcn_sched_barrier(0);
-        compute_visit<D>(c, k, buf_a, ca, qraw, cf0, cf1, o, m, l, lane);
-        if (seam_first && k == 0) {          // back to R(t) after the seam visit
-            load_coef<D>(g.table, c.tb0, gq, cf0);
-            load_coef<D>(g.table, c.tb1, gq, cf1);
+        DecK<D> rk;
+        u32x4 rv[NB];
+        wait_k(k);
+        dec_read_k<D>(c, ka, rk);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);                                 // copied out of ka
+        if (k + 8 < k1) dec_load_k<D>(c, k + 8, lane, ka);
+        bf16x8 pb;
+        if (k == 0 && c.t_o > 0) {      // the seam visit (a wave-uniform branch)
+            float4 rw[D / 64][4], s0c[D / 64][4], s1c[D / 64][4];
+            lds_coef<D>(lds_rw, gq, rw);
+            seam_coef<D>(rw, cf0, c.tb0 < c.t_o, s0c);
+            seam_coef<D>(rw, cf1, c.tb1 < c.t_o, s1c);
+            pb = dec_scores<D>(c, k, rk, qraw, s0c, s1c, o, m, l);
+        } else {
+            pb = dec_scores<D>(c, k, rk, qraw, cf0, cf1, o, m, l);
         }
-        k = kn;
+        wait_v(k);
+        dec_read_v<D>(va, lane, rv);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        if (k + 8 < k1) dec_load_v<D>(c, k + 8, va);
+        dec_pv<D>(rv, pb, o);
+        k += 4;
         if (k >= k1) break;
-        kn = k + 4;
-        load_visit<D>(c, kn < k1 ? kn : k, buf_a, ca);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerVisit));
-        __builtin_amdgcn_sched_barrier(0);
-        compute_visit<D>(c, k, buf_b, cb, qraw, cf0, cf1, o, m, l, lane);
-        k = kn;
+        wait_k(k);
+        dec_read_k<D>(c, kb, rk);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        if (k + 8 < k1) dec_load_k<D>(c, k + 8, lane, kb);
+        pb = dec_scores<D>(c, k, rk, qraw, cf0, cf1, o, m, l);
+        wait_v(k);
+        dec_read_v<D>(vb, lane, rv);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        if (k + 8 < k1) dec_load_v<D>(c, k + 8, vb);
+        dec_pv<D>(rv, pb, o);
+        k += 4;
     }
-    __builtin_amdgcn_s_waitcnt(0);   // the last prefetch lands before the LDS is reused
+    __builtin_amdgcn_s_waitcnt(0);   // every load has landed before the LDS is reused
+    lds_fence();
+
+    if (fused && kh == 0 && split == 0 && tid == 0) {   // record of the new state
+        DevState ns;
+        ns.next_pos = st.next_pos[bi] + 1;
+        ns.length = L;
+        ns.next_slot = next_slot;
+        g.state[(int64_t)layer * g.n_streams + b] = ns;
+    }
 
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
