@@ -88,13 +88,12 @@ __global__ void reset_kernel(Geometry g, StreamBatch r) {
 // K rows are row-major; element d of V for slot s lives at ((s/8)*D + d)*8 + s%8
 // of the head's V block array.
 template <int EB>
-__device__ __forceinline__ void write_token(const Geometry& g, int64_t pair, int slot, int c,
-                                            const uint8_t* ksrc, const uint8_t* vsrc) {
+__device__ __forceinline__ void write_token_vals(const Geometry& g, int64_t pair, int slot, int c, u32x4 kv,
+                                                 u32x4 vv) {
     constexpr int per16 = 16 / EB;
     const int D = g.d;
     uint8_t* kdst = (uint8_t*)g.k_ring + ((pair * g.w_pad + slot) * D + (int64_t)c * per16) * EB;
-    *(u32x4*)kdst = *(const u32x4*)ksrc;
-    const u32x4 vv = *(const u32x4*)vsrc;
+    *(u32x4*)kdst = kv;
     uint8_t* vblk = (uint8_t*)g.v_ring + ((pair * (g.w_pad / 8) + slot / 8) * (int64_t)D * 8) * EB;
     const int lane8 = slot & 7;
 #pragma unroll
@@ -107,6 +106,12 @@ __device__ __forceinline__ void write_token(const Geometry& g, int64_t pair, int
             ((uint32_t*)vblk)[(int64_t)d * 8 + lane8] = vv[u];
         }
     }
+}
+
+template <int EB>
+__device__ __forceinline__ void write_token(const Geometry& g, int64_t pair, int slot, int c,
+                                            const uint8_t* ksrc, const uint8_t* vsrc) {
+    write_token_vals<EB>(g, pair, slot, c, *(const u32x4*)ksrc, *(const u32x4*)vsrc);
 }
 
 // One block per stream; token j of stream b goes to slot (S + j) mod W.
@@ -607,6 +612,27 @@ __device__ __forceinline__ void dec_pv(const u32x4 (&v)[D / 16], bf16x8 pb, floa
         o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[nb]), pb, o[nb], 0, 0, 0);
 }
 
+// The new token (fused append) written into the LDS copy of its tile: K row t
+// (16-byte chunk `lane` of dims 8*lane ..) and element t % 8 of the
+// transposed V chunks of block t / 8.
+template <int D>
+__device__ __forceinline__ void patch_k(unsigned char* kbuf, int t, int lane, u32x4 tk) {
+    if (lane < D / 8) *(u32x4*)(kbuf + 16 * k_pos<D>(t, lane)) = tk;
+}
+
+template <int D>
+__device__ __forceinline__ void patch_v(unsigned char* vbuf, int t, int lane, u32x4 tv) {
+    if (lane < D / 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int d = 8 * lane + u;
+            const uint32_t w = tv[u >> 1];
+            *(uint16_t*)(vbuf + (d >> 4) * 1024 + 16 * ((d & 15) + 16 * (t >> 3)) + 2 * (t & 7)) =
+                (uint16_t)((u & 1) ? (w >> 16) : (w & 0xffffu));
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, StreamBatch st,
                                                       const uint16_t* __restrict__ q,
@@ -624,6 +650,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     __shared__ __align__(16) unsigned char lds_rt[kTile * D * 4];
     __shared__ __align__(16) unsigned char lds_q[4096];
     __shared__ __align__(16) unsigned char lds_rw[1024];
+    __shared__ __align__(16) unsigned char lds_tok[1024];
     __shared__ float red_ml[4][16][2];
     __shared__ int s_last;
     static_assert(4 * 16 * D * 4 <= 4 * B::kK, "merge buffer does not fit");
@@ -675,15 +702,25 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     const int per = (n_visit + n_split - 1) / n_split;
     const int k0 = split * per, k1 = min(n_visit, k0 + per);
 
+    // Fused append: the wave whose visits include the new token's tile (visit
+    // k_tok) loads the token into LDS with its prologue, patches it into its LDS
+    // copy of that tile once the tile has landed, and writes it into the ring
+    // slot after the walk, so nothing waits for a store (no other wave or block
+    // reads that slot in this call).
+    int k_tok = -1;
+    const int t_tok = s_prev & (kTile - 1);
     if (fused) {
-        // the wave whose visits include the new token's tile writes the token
         int kv = s_prev / kTile - c.p0t;
         if (kv < 0) kv += c.n_tiles;
-        if (kv >= k0 && kv < k1 && (kv - k0) % 4 == wave && lane < D / 8) {
-            const int64_t src = (((int64_t)bi * g.hkv + kh) * D + lane * 8) * 2;
-            write_token<2>(g, pair, s_prev, lane, (const uint8_t*)k_new + src, (const uint8_t*)v_new + src);
+        if (kv >= k0 && kv < k1 && (kv - k0) % 4 == wave) {
+            // at most one wave per block: the token's K row to lds_tok[0, 2D),
+            // its V row to [2D, 4D) (other lanes re-read the K row's start)
+            k_tok = kv;
+            const int64_t src = ((int64_t)bi * g.hkv + kh) * D;
+            const uint16_t* from = lane < D / 8 ? k_new + src + 8 * lane
+                                 : lane < D / 4 ? v_new + src + 8 * (lane - D / 8) : k_new + src;
+            dma16(from, lds_tok + 16 * lane);
         }
-        __builtin_amdgcn_s_waitcnt(0);
     }
 
     // Prologue, every load a direct global->LDS load (so the explicit wait
@@ -761,6 +798,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         DecK<D> rk;
         u32x4 rv[NB];
         wait_k(k);
+        if (k == k_tok) patch_k<D>(ka, t_tok, lane, ((const u32x4*)lds_tok)[lane & (D / 8 - 1)]);
         dec_read_k<D>(c, ka, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);                                 // copied out of ka
         if (k + 8 < k1) dec_load_k<D>(c, k + 8, lane, ka);
@@ -775,6 +813,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             pb = dec_scores<D>(c, k, rk, qraw, cf0, cf1, o, m, l);
         }
         wait_v(k);
+        if (k == k_tok) patch_v<D>(va, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(va, lane, rv);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         if (k + 8 < k1) dec_load_v<D>(c, k + 8, va);
@@ -782,11 +821,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         k += 4;
         if (k >= k1) break;
         wait_k(k);
+        if (k == k_tok) patch_k<D>(kb, t_tok, lane, ((const u32x4*)lds_tok)[lane & (D / 8 - 1)]);
         dec_read_k<D>(c, kb, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         if (k + 8 < k1) dec_load_k<D>(c, k + 8, lane, kb);
         pb = dec_scores<D>(c, k, rk, qraw, cf0, cf1, o, m, l);
         wait_v(k);
+        if (k == k_tok) patch_v<D>(vb, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(vb, lane, rv);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         if (k + 8 < k1) dec_load_v<D>(c, k + 8, vb);
@@ -795,6 +836,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     }
     __builtin_amdgcn_s_waitcnt(0);   // every load has landed before the LDS is reused
     lds_fence();
+
+    if (k_tok >= 0 && lane < D / 8)     // the new token into its ring slot, for later calls
+        write_token_vals<2>(g, pair, s_prev, lane, ((const u32x4*)lds_tok)[lane], ((const u32x4*)lds_tok)[D / 8 + lane]);
 
     if (fused && kh == 0 && split == 0 && tid == 0) {   // record of the new state
         DevState ns;
