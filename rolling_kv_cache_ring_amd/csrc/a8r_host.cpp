@@ -115,7 +115,7 @@ struct Ledger {
 };
 
 struct Layout {
-    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, counter_off, total;
+    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, counter_off, part_t_off, total;
     int w_pad, rows_max;
 };
 
@@ -176,6 +176,10 @@ a8r_status compute_layout(const a8r_config* c, Layout* lay) {
     lay->counter_off = off;
     off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kMaxRowGroups * sizeof(int),
                         a8r::kAlign);
+    lay->part_t_off = off;
+    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kMaxSplits * a8r::kMaxGroupTagged *
+                                  (c->head_dim + 2) * sizeof(uint64_t),
+                        a8r::kAlign);
     lay->total = off;
     lay->w_pad = w_pad;
     lay->rows_max = rows_max;
@@ -213,6 +217,7 @@ struct a8r_cache {
     a8r::Geometry geo{};
     hipStream_t stream = nullptr;
     void* base = nullptr;
+    mutable uint32_t epoch = 0;   // launch counter; tags decode split partials (never 0)
     bool owns = false;
     bool poisoned = false;
     int device = 0;
@@ -307,6 +312,7 @@ a8r_status a8r_cache_create(const a8r_config* cfg, void* hip_stream, void* works
     g.part_o = (float*)(b + lay.part_o_off);
     g.part_ml = (float*)(b + lay.part_ml_off);
     g.counters = (int*)(b + lay.counter_off);
+    g.part_t = (uint64_t*)(b + lay.part_t_off);
     g.n_layers = cfg->n_layers;
     g.n_streams = cfg->n_streams;
     g.hq = cfg->n_q_heads;
@@ -358,6 +364,8 @@ namespace {
 void fill_batch(const a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, a8r::StreamBatch* sb) {
     sb->b0 = b0;
     sb->nb = nb;
+    if (++c->epoch == 0) c->epoch = 1;   // the workspace starts zeroed: tag 0 never matches
+    sb->epoch = c->epoch;
     for (int32_t i = 0; i < nb; ++i) {
         const PairState& p = c->ledger.at(layer, b0 + i);
         sb->next_slot[i] = p.next_slot;

@@ -33,6 +33,7 @@ constexpr int kMaxPartialQ = 16;   // chunk sizes above this run without splits
 constexpr size_t kAlign = 256;
 constexpr int kBatch = 128;        // streams per launch (their state travels in the arguments)
 constexpr int kMaxRowGroups = 4;   // query row groups of one KV head in the chunk kernel
+constexpr int kMaxGroupTagged = 16; // query heads per KV head in the MFMA decode kernel
 
 struct DevState {
     int64_t next_pos;   // absolute position of the next token
@@ -44,6 +45,7 @@ struct DevState {
 // host bookkeeping holds it when the call is made.
 struct StreamBatch {
     int b0, nb;
+    uint32_t epoch;     // nonzero, different for every launch of a cache (tags split partials)
     int32_t next_slot[kBatch];
     int32_t length[kBatch];
     int64_t next_pos[kBatch];
@@ -58,6 +60,8 @@ struct Geometry {
     float* part_o;      // split partials: [n_streams][n_kv_heads][kMaxSplits][rows_max][D]
     float* part_ml;     // [n_streams][n_kv_heads][kMaxSplits][rows_max][2]
     int* counters;      // [n_streams][n_kv_heads][kMaxRowGroups] split arrival counters, 0 between calls
+    uint64_t* part_t;   // decode split partials tagged with the launch epoch (high word):
+                        // [n_streams][n_kv_heads][kMaxSplits][kMaxGroupTagged][D + 2] (O..., m, l)
     int n_layers, n_streams, hq, hkv, group, d, window, w_pad;
     int elem_bytes;     // 2 (bf16) or 4 (f32)
     int rows_max;       // max(1, min(max_chunk, kMaxPartialQ)) * group

@@ -862,7 +862,25 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             for (int j = 0; j < 4; ++j) red_o[wave][n][16 * nb + 4 * gq + j] = o[nb][j];
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += 256) {
+
+    // The block's partial {m, l, O} for each (head, dim) this thread owns.
+    // Splits publish partials as (value, epoch) pairs with single 64-bit
+    // agent-coherent stores and count themselves in right away; the last block
+    // to arrive merges, re-reading any element whose tag is not yet this
+    // launch's (the stores are already in flight, so the wait is bounded).  The
+    // merge sums the splits in index order whichever block does it, so results
+    // are the same run to run.
+    constexpr int kPer = (kMaxGroupTagged * D + 255) / 256;
+    float p_num[kPer], p_den[kPer], p_m[kPer];
+    const uint32_t epoch = st.epoch;
+    auto tagged = [&](float x) { return ((uint64_t)epoch << 32) | __float_as_uint(x); };
+    auto trow = [&](int sp, int h) {
+        return g.part_t + ((((int64_t)bi * g.hkv + kh) * kMaxSplits + sp) * kMaxGroupTagged + h) * (D + 2);
+    };
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int idx = tid + 256 * i;
+        if (idx >= G * D) break;
         const int h = idx / D, d = idx - h * D;
         float mm = red_ml[0][h][0];
 #pragma unroll
@@ -874,25 +892,23 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             num += f * red_o[w][h][d];
             den += f * red_ml[w][h][1];
         }
+        p_num[i] = num;
+        p_den[i] = den;
+        p_m[i] = mm;
         if (n_split == 1) {
             out[((int64_t)bi * g.hq + kh * G + h) * D + d] = f32_to_bf16_bits(num / den);
         } else {
-            // agent-coherent stores: visible to the merging block on any XCD
-            // once they have completed, without a cache writeback
-            const int64_t pr = part_row(g, bi, kh, split, h);
-            __hip_atomic_store(&g.part_o[pr * D + d], num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint64_t* pr = trow(split, h);
+            __hip_atomic_store(pr + d, tagged(num), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (d == 0) {
-                __hip_atomic_store(&g.part_ml[pr * 2], mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&g.part_ml[pr * 2 + 1], den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(pr + D, tagged(mm), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(pr + D + 1, tagged(den), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
     if (n_split == 1) return;
 
-    // wait until this thread's partial stores have completed, then count the
-    // block in; the last block of the pair merges every split's partials
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    __syncthreads();            // every store of the block has been issued
     int* counter = &g.counters[(bi * g.hkv + kh) * kMaxRowGroups];
     if (tid == 0) {
         const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -900,21 +916,75 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     }
     __syncthreads();
     if (!s_last) return;
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int h = idx / D, d = idx - h * D;
-        float mm = kNegBig;
-        for (int sp = 0; sp < n_split; ++sp)
-            mm = fmaxf(mm, __hip_atomic_load(&g.part_ml[part_row(g, bi, kh, sp, h) * 2], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT));
-        float num = 0.f, den = 0.f;
-        for (int sp = 0; sp < n_split; ++sp) {
-            const int64_t pr = part_row(g, bi, kh, sp, h);
-            const float f =
-                exp2f(__hip_atomic_load(&g.part_ml[pr * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - mm);
-            den += f * __hip_atomic_load(&g.part_ml[pr * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            num += f * __hip_atomic_load(&g.part_o[pr * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Merge: splits in index order, an online combination per element
+    // (running max, numerator, denominator).  For each other split, the loads
+    // of all of this thread's elements are issued together; an element whose
+    // tag is not yet this launch's is re-read (its store is in flight).  A
+    // value that never arrives (impossible unless memory is corrupted) becomes
+    // NaN after a bounded number of retries instead of hanging.
+    float r_m[kPer], r_num[kPer], r_den[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        r_m[i] = kNegBig;
+        r_num[i] = 0.f;
+        r_den[i] = 0.f;
+    }
+    const int n_mine = (G * D - tid + 255) / 256;       // elements of this thread
+    for (int sp = 0; sp < n_split; ++sp) {
+        float vm[kPer], vl[kPer], vo[kPer];
+        if (sp == split) {
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                vm[i] = p_m[i];
+                vl[i] = p_den[i];
+                vo[i] = p_num[i];
+            }
+        } else {
+            uint64_t tm[kPer], tl[kPer], to[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                if (i >= n_mine) break;
+                const int idx = tid + 256 * i, h = idx / D, d = idx - h * D;
+                const uint64_t* pr = trow(sp, h);
+                tm[i] = __hip_atomic_load(pr + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                tl[i] = __hip_atomic_load(pr + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                to[i] = __hip_atomic_load(pr + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                if (i >= n_mine) break;
+                const int idx = tid + 256 * i, h = idx / D, d = idx - h * D;
+                const uint64_t* pr = trow(sp, h);
+                bool ok = false;
+                for (int spin = 0; spin < (1 << 16); ++spin) {
+                    ok = (uint32_t)(tm[i] >> 32) == epoch && (uint32_t)(tl[i] >> 32) == epoch &&
+                         (uint32_t)(to[i] >> 32) == epoch;
+                    if (ok) break;
+                    __builtin_amdgcn_s_sleep(1);
+                    tm[i] = __hip_atomic_load(pr + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    tl[i] = __hip_atomic_load(pr + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    to[i] = __hip_atomic_load(pr + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                vm[i] = __uint_as_float((uint32_t)tm[i]);
+                vl[i] = ok ? __uint_as_float((uint32_t)tl[i]) : __uint_as_float(0x7fc00000u);
+                vo[i] = __uint_as_float((uint32_t)to[i]);
+            }
         }
-        out[((int64_t)bi * g.hq + kh * G + h) * D + d] = f32_to_bf16_bits(num / den);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            if (i >= n_mine) break;
+            const float mn = fmaxf(r_m[i], vm[i]);
+            const float a = exp2f(r_m[i] - mn), f = exp2f(vm[i] - mn);
+            r_num[i] = r_num[i] * a + vo[i] * f;
+            r_den[i] = r_den[i] * a + vl[i] * f;
+            r_m[i] = mn;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        if (i >= n_mine) break;
+        const int idx = tid + 256 * i, h = idx / D, d = idx - h * D;
+        out[((int64_t)bi * g.hq + kh * G + h) * D + d] = f32_to_bf16_bits(r_num[i] / r_den[i]);
     }
     if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
