@@ -346,19 +346,6 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 // the new token's tile writes the token into its ring slot before it reads that
 // tile (no other wave touches that slot).
 
-// Used by the chunk kernel: one buffer holds a visit's K rows (2*(D/32) 1-KiB
-// chunks, lane l's 16 bytes at 16*l) and V blocks (D/16 chunks).
-template <int D>
-struct DecodeLds {
-    static constexpr int kChunks = 2 * (D / 32) + D / 16;
-    static constexpr int kBytes = kChunks * 1024;
-};
-
-template <int D>
-struct DecodeCoef {
-    float4 qc[D / 64][4];   // (cos, sin) pairs of R(r_q - rho) for this lane's query dims
-};
-
 struct DecodeCtx {
     const uint16_t* kp;
     const uint16_t* vp;
@@ -477,7 +464,10 @@ __device__ __forceinline__ void dma_table_row(const float2* table, int row, int 
     dma16((const unsigned char*)(table + (int64_t)row * (D / 2)) + off, dst);
 }
 
-template <int D>
+// The coefficient row staged after the K rows: R(r_q - rho) for decode (the
+// query's rotation for this visit); for the chunk kernel R(rho), or R(t_o) on
+// the first visit (rho = -t_o, used conjugated).
+template <int D, bool CHUNK = false>
 __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, unsigned char* kbuf) {
     constexpr int RPI = 64 / (D / 8);            // rows per instruction
     const int p = visit_tile(c, k);
@@ -489,7 +479,8 @@ __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, 
         const int col = 8 * (sl >> 3) + ((sl & 7) ^ k_swz(r));
         dma16(c.kp + (int64_t)(s0 + r) * D + 8 * col, kbuf + j * 1024);
     }
-    dma_table_row<D>(c.table, c.rq - visit_rho(c, k, s0), lane, kbuf + 2 * (D / 32) * 1024);
+    const int rho = visit_rho(c, k, s0);
+    dma_table_row<D>(c.table, CHUNK ? (rho < 0 ? -rho : rho) : c.rq - rho, lane, kbuf + 2 * (D / 32) * 1024);
 }
 
 template <int D>
@@ -991,29 +982,29 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
 
 // ------------------------------------------------------------- MFMA chunk ----
 // bf16 attention for C new positions per stream (several per audio clock) in
-// one block per (stream, KV head, split): the C x G query rows of a KV head
-// (row = c*G + hg) form NQ column blocks of 16, so QK^T and PV are real
-// contractions on v_mfma_f32_16x16x32_bf16 (64 rows for 8 positions x 8 heads).
+// one block per (stream, KV head, split) and group of up to 64 query rows: the
+// C x G query rows of a KV head (row = c*G + hg) form NQ column blocks of 16, so
+// QK^T and PV are real contractions on v_mfma_f32_16x16x32_bf16 (8 positions x
+// 8 heads = 64 rows, NQ = 4, in one block: every K/V tile is read once).
 //
-// Same ring walk, LDS staging and split merge as decode_mfma.  The rotation is
-// split differently: each query row is rotated once, by its own re-based index
-// r_q(c) = L - C + c; each key row is rotated by R(rho + t), composed per
-// visit from R(rho) (a table row fetched with the visit) and R(t) (t < 32,
-// staged in LDS):  (c, s)(a + b) = (c_a c_b - s_a s_b, s_a c_b + c_a s_b).
-// Query c sees keys with index <= r_q(c): causal inside the chunk, the whole
-// older window before it.  The first visit (rho = -t_o, and rho + W for the
-// window's newest keys sharing the oldest key's tile) reads its key rotations
-// straight from the table rows of the keys' indices.
+// Same ring walk, memory pipeline (LDS DMA, K and V parts, exact waits) and
+// split merge as decode_mfma.  The rotation is split differently: each query
+// row is rotated once, by its own re-based index r_q(c) = L - C + c, in the
+// prologue; each key row is rotated by R(rho + t), composed per visit from
+// R(rho) (the table row staged with the visit's K part) and the lane's R(t)
+// (registers):  (c, s)(a + b) = (c_a c_b - s_a s_b, s_a c_b + c_a s_b).  On the
+// first visit rho = -t_o: R(-t_o) is R(t_o) conjugated, and the window's newest
+// keys that share the oldest key's tile (offsets t < t_o, index t - t_o + W)
+// get R(W) composed on top.  Query c sees keys with index <= r_q(c): causal
+// inside the chunk, the whole older window before it.
 template <int D>
-__device__ __forceinline__ void compose(const float4 (&a)[D / 64][4], const float2* __restrict__ bt,
+__device__ __forceinline__ void compose(const float4 (&a)[D / 64][4], const float4 (&b)[D / 64][4],
                                         float4 (&out)[D / 64][4]) {
-    // bt: this lane's R(t) pairs in LDS (dims 8*gq + 32*kk + e), as float2
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float4 x = a[kk][j];
-            const float4 y = *(const float4*)(bt + 32 * kk + 2 * j);
+            const float4 x = a[kk][j], y = b[kk][j];
             out[kk][j] = float4{x.x * y.x - x.y * y.y, x.y * y.x + x.x * y.y,
                                 x.z * y.z - x.w * y.w, x.w * y.z + x.z * y.w};
         }
@@ -1025,25 +1016,28 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
                                                      uint16_t* __restrict__ out, int n_split) {
     // NQ column blocks of 16 query rows per block; row group rg covers rows
     // 16*NQ*rg .. 16*NQ*(rg+1)-1 (blockIdx.x = rg * n_split + split)
-    constexpr int KK = D / 32, NB = D / 16, NP = D / 2, HP = D / 64;
-    constexpr int kBuf = DecodeLds<D>::kBytes;
-    constexpr int kLoadsPerVisit = DecodeLds<D>::kChunks + 4 * HP;
+    constexpr int KK = D / 32, NB = D / 16, HP = D / 64;
+    using B = DecBuf<D>;
     constexpr int kRows = 16 * NQ;
-    // LDS: per wave two visit buffers (two distinct objects), the rotated query
-    // rows in MFMA B-operand order (shared by the 4 waves), R(t) for t < 32.
-    // After the walk the visit buffers hold the cross-wave merge and the query
-    // area holds the per-row (m, l) values.
-    __shared__ __align__(16) unsigned char lds_tiles_a[4 * kBuf];
-    __shared__ __align__(16) unsigned char lds_tiles_b[4 * kBuf];
+    constexpr int kHalf = 4 * (B::kK + B::kV);   // buffers a (K, V) of the 4 waves; then b
+    // LDS: the visit buffers of the 4 waves (buffer b also stages the prologue
+    // inputs; after the walk the array holds the cross-wave merge), the
+    // rotated query rows in MFMA B-operand order (after the walk: the per-row
+    // (m, l) values), the R(W) row.
+    __shared__ __align__(16) unsigned char lds_kv[2 * kHalf];
     __shared__ __align__(16) unsigned char q_lds[NQ * KK * 1024];
-    __shared__ __align__(16) float2 rt_lds[kTile * NP];
-    static_assert(4 * kRows * D * 4 <= 8 * kBuf, "merge buffer does not fit");
-    static_assert(4 * kRows * 2 * 4 + 16 <= NQ * KK * 1024, "(m, l) buffer does not fit");
-    float (*red_o)[kRows][D] = (float (*)[kRows][D])lds_tiles_a;   // spans both tile arrays
+    __shared__ __align__(16) unsigned char lds_rw[1024];
+    __shared__ int s_last;
+    static_assert(4 * kRows * D * 4 <= 2 * kHalf, "merge buffer does not fit");
+    static_assert(4 * kRows * 2 * 4 <= NQ * KK * 1024, "(m, l) buffer does not fit");
+    // staging in buffer b: raw query rows, R(r_q(c)) rows (1 KiB slots), R(t) rows
+    constexpr int kStQ = 0, kStRc = kRows * D * 2, kStRt = kStRc + kMaxPartialQ * 1024;
+    static_assert(kStRt + kTile * D * 4 <= kHalf, "staging does not fit");
+    float (*red_o)[kRows][D] = (float (*)[kRows][D])lds_kv;
     float (*red_ml)[kRows][2] = (float (*)[kRows][2])q_lds;
-    int* s_last = (int*)(q_lds + 4 * kRows * 2 * 4);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, gq = lane >> 4;
     const int bi = blockIdx.z, kh = blockIdx.y;
     const int rg = blockIdx.x / n_split, split = blockIdx.x - rg * n_split;
@@ -1051,8 +1045,11 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
     const int rows = C * G;                       // query rows of this KV head
     const int row0 = rg * kRows;                  // first row of this block
     const int n_rows = min(kRows, rows - row0);   // rows this block handles
-    unsigned char* buf_a = lds_tiles_a + wave * kBuf;
-    unsigned char* buf_b = lds_tiles_b + wave * kBuf;
+    unsigned char* ka = lds_kv + wave * B::kK;
+    unsigned char* va = lds_kv + 4 * B::kK + wave * B::kV;
+    unsigned char* kb = lds_kv + kHalf + wave * B::kK;
+    unsigned char* vb = lds_kv + kHalf + 4 * B::kK + wave * B::kV;
+    unsigned char* stage = lds_kv + kHalf;
 
     DecodeCtx c;
     const int L = st.length[bi];
@@ -1085,45 +1082,49 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
     }
     const int per = (n_visit + n_split - 1) / n_split;
     const int k0 = split * per, k1 = min(n_visit, k0 + per);
-
-    // Issues a visit's loads: K/V into the LDS buffer, R(rho) into registers
-    // (visits after the first; rho >= 0 there).
-    auto issue = [&](int kv, unsigned char* buf, DecodeCoef<D>& t) {
-        const int p = visit_tile(c, kv);
-        const int s0 = p * kTile;
-        const uint16_t* r0 = c.kp + (int64_t)(s0 + c.tb0) * D + 8 * gq;
-        const uint16_t* r1 = c.kp + (int64_t)(s0 + c.tb1) * D + 8 * gq;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            __builtin_amdgcn_global_load_lds((const void*)(r0 + 32 * kk), (lds_void*)(buf + kk * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(r1 + 32 * kk), (lds_void*)(buf + (KK + kk) * 1024), 16,
-                                             0, 0);
-        }
-        const uint16_t* vb = c.vp + ((int64_t)(p * 4 + gq) * D + n) * 8;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)nb * 16 * 8),
-                                             (lds_void*)(buf + (2 * KK + nb) * 1024), 16, 0, 0);
-        load_coef<D>(c.table, kv == 0 ? 0 : visit_rho(c, kv, s0), gq, t.qc);
-    };
-    DecodeCoef<D> ca, cb;
     int k = k0 + wave;
-    if (k < k1) issue(k, buf_a, ca);
 
-    for (int idx = tid; idx < kTile * NP; idx += 256) rt_lds[idx] = g.table[idx];
-    // wave w rotates query column block w (rows 16w .. 16w+15 of the block) by
-    // R(L - C + c) and stores it in B-operand order
-    if (wave < NQ) {
-        const int row = row0 + 16 * wave + n;
+    // Prologue (all LDS DMA): the block's raw query rows (rows past the chunk
+    // re-read row 0), the rows R(r_q(c)), R(t) for t < 32 and R(W), spread over
+    // the waves; then K(k), V(k); wait; every wave's.
+    {
+        constexpr int nq = kRows * D * 2 / 1024;
+        for (int j = wave; j < nq; j += 4) {
+            const int byte = j * 1024 + 16 * lane;
+            const int lr = byte / (D * 2), off = byte - lr * (D * 2);
+            int row = row0 + lr;
+            if (row >= rows) row = 0;
+            const int cc = row / G, h = kh * G + (row - cc * G);
+            dma16((const unsigned char*)(q + (((int64_t)bi * C + cc) * g.hq + h) * D) + off, stage + kStQ + j * 1024);
+        }
+        for (int cc = wave; cc < C; cc += 4) dma_table_row<D>(g.table, c.rq + cc, lane, stage + kStRc + cc * 1024);
+        constexpr int nrt = kTile * D * 4 / 1024;
+        for (int j = wave; j < nrt; j += 4)
+            dma16((const unsigned char*)g.table + j * 1024 + 16 * lane, stage + kStRt + j * 1024);
+        if (wave == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
+    }
+    if (k < k1) {
+        dec_load_k<D, true>(c, k, lane, ka);
+        dec_load_v<D>(c, k, va);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
+    } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    lds_fence();
+
+    // each wave rotates query column blocks cq = wave, wave + 4, ... by
+    // R(L - C + c) into q_lds (B-operand order); every lane keeps R(t) of its
+    // two key offsets
+    for (int cq = wave; cq < NQ; cq += 4) {
+        const int lr = 16 * cq + n, row = row0 + lr;
         bf16x8 qb[KK];
         if (row < rows) {
-            const int cc = row / G, h = kh * G + (row - cc * G);
-            const uint16_t* qp = q + (((int64_t)bi * C + cc) * g.hq + h) * D + 8 * gq;
             u32x4 qr[KK];
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) qr[kk] = *(const u32x4*)(qp + 32 * kk);
+            for (int kk = 0; kk < KK; ++kk) qr[kk] = *(const u32x4*)(stage + kStQ + lr * D * 2 + 16 * gq + 64 * kk);
             float4 cq4[HP][4];
-            load_coef<D>(g.table, c.rq + cc, gq, cq4);
+            lds_coef<D>(stage + kStRc + (row / G) * 1024, gq, cq4);
             rotate_row<D>(cq4, qr, qb);
         } else {
 #pragma unroll
@@ -1132,9 +1133,11 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
                 for (int e = 0; e < 8; ++e) qb[kk][e] = (__bf16)0.f;
         }
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            *((bf16x8*)(q_lds + (wave * KK + kk) * 1024) + lane) = qb[kk];
+        for (int kk = 0; kk < KK; ++kk) *((bf16x8*)(q_lds + (cq * KK + kk) * 1024) + lane) = qb[kk];
     }
+    float4 cf0[HP][4], cf1[HP][4];
+    lds_coef<D>(stage + kStRt + c.tb0 * D * 4, gq, cf0);
+    lds_coef<D>(stage + kStRt + c.tb1 * D * 4, gq, cf1);
     // each column's query index for the causal mask (-1: padding row)
     int rq_col[NQ];
 #pragma unroll
@@ -1142,7 +1145,11 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
         const int row = row0 + 16 * cq + n;
         rq_col[cq] = row < rows ? c.rq + row / G : -1;
     }
-    __syncthreads();   // rt_lds and q_lds ready
+    __syncthreads();   // q_lds ready, staging consumed
+    if (k + 4 < k1) {
+        dec_load_k<D, true>(c, k + 4, lane, kb);
+        dec_load_v<D>(c, k + 4, vb);
+    }
 
     floatx4 o[NQ][NB];
 #pragma unroll
@@ -1157,30 +1164,44 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
     }
     const int r_last = L - 1;   // the newest query's index
 
-    auto compute = [&](int kv, const unsigned char* buf, const DecodeCoef<D>& t) {
+    // scores of visit k for every column block, online softmax; probabilities
+    // (keys 8*gq .. 8*gq+7 of each column) in pb
+    auto scores = [&](int kv, const DecK<D>& rk, bf16x8 (&pb)[NQ]) {
         const int p = visit_tile(c, kv);
         const int s0 = p * kTile;
         const int rho = visit_rho(c, kv, s0);
         const bool seam = (kv == 0) && (c.t_o > 0);
-        const u32x4* lb = (const u32x4*)buf + lane;
-        bf16x8 kb[2][KK];
+        float4 base[HP][4], ca[HP][4], cb[HP][4];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int tt = bb ? c.tb1 : c.tb0;
-            float4 cf[HP][4];
-            if (kv == 0) {
-                // key index r = tt - t_o, or tt - t_o + W before the oldest slot
-                int r = tt - c.t_o;
-                if (seam && tt < c.t_o) r += W;
-                load_coef<D>(c.table, r < 0 ? 0 : r, gq, cf);
-            } else {
-                compose<D>(t.qc, rt_lds + tt * NP + 8 * gq, cf);
+        for (int kk = 0; kk < HP; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 x = rk.qc[kk][j];
+                base[kk][j] = kv == 0 ? float4{x.x, -x.y, x.z, -x.w} : x;   // R(-t_o) or R(rho)
             }
-            u32x4 kr[KK];
+        compose<D>(base, cf0, ca);
+        compose<D>(base, cf1, cb);
+        if (seam) {
+            float4 rw[HP][4], t[HP][4];
+            lds_coef<D>(lds_rw, gq, rw);
+            if (c.tb0 < c.t_o) {
+                compose<D>(rw, ca, t);
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) kr[kk] = lb[(bb * KK + kk) * 64];
-            rotate_row<D>(cf, kr, kb[bb]);
+                for (int kk = 0; kk < HP; ++kk)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ca[kk][j] = t[kk][j];
+            }
+            if (c.tb1 < c.t_o) {
+                compose<D>(rw, cb, t);
+#pragma unroll
+                for (int kk = 0; kk < HP; ++kk)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) cb[kk][j] = t[kk][j];
+            }
         }
+        bf16x8 k0b[KK], k1b[KK];
+        rotate_row<D>(ca, rk.k0, k0b);
+        rotate_row<D>(cb, rk.k1, k1b);
         const bool full = (kv != 0) && (rho + kTile <= c.rq + 1) && (s0 + kTile <= W);
         const bf16x8* qlb = (const bf16x8*)q_lds + lane;
 #pragma unroll
@@ -1189,8 +1210,8 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 const bf16x8 qv = qlb[(cq * KK + kk) * 64];
-                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[0][kk], qv, a0, 0, 0, 0);
-                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[1][kk], qv, a1, 0, 0, 0);
+                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0b[kk], qv, a0, 0, 0, 0);
+                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1b[kk], qv, a1, 0, 0, 0);
             }
             float s[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
@@ -1218,38 +1239,65 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
                 for (int i = 0; i < NB; ++i) o[cq][i] *= alpha;
                 m[cq] = mx;
             }
-            bf16x8 pb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float pe = exp2f(s[e] - m[cq]);
                 l[cq] += pe;
-                pb[e] = (__bf16)pe;
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const u32x4 vv = lb[(2 * KK + nb) * 64];
-                o[cq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb, o[cq][nb],
-                                                                    0, 0, 0);
+                pb[cq][e] = (__bf16)pe;
             }
         }
     };
-
+    auto pv = [&](const u32x4 (&v)[NB], const bf16x8 (&pb)[NQ]) {
+#pragma unroll
+        for (int cq = 0; cq < NQ; ++cq)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                o[cq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[nb]), pb[cq],
+                                                                    o[cq][nb], 0, 0, 0);
+    };
+    auto wait_k = [&](int kk) {
+        if (kk + 4 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV + B::nK + B::nV));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
+        __builtin_amdgcn_sched_barrier(0);
+        lds_fence();
+    };
+    auto wait_v = [&](int kk) {
+        if (kk + 8 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nK + B::nV + B::nK));
+        else if (kk + 4 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nK + B::nV));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_sched_barrier(0);
+        lds_fence();
+    };
     while (k < k1) {
-        int kn = k + 4;
-        issue(kn < k1 ? kn : k, buf_b, cb);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerVisit));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(k, buf_a, ca);
-        k = kn;
+        DecK<D> rk;
+        u32x4 rv[NB];
+        bf16x8 pb[NQ];
+        wait_k(k);
+        dec_read_k<D>(c, ka, rk);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        if (k + 8 < k1) dec_load_k<D, true>(c, k + 8, lane, ka);
+        scores(k, rk, pb);
+        wait_v(k);
+        dec_read_v<D>(va, lane, rv);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        if (k + 8 < k1) dec_load_v<D>(c, k + 8, va);
+        pv(rv, pb);
+        k += 4;
         if (k >= k1) break;
-        kn = k + 4;
-        issue(kn < k1 ? kn : k, buf_a, ca);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerVisit));
-        __builtin_amdgcn_sched_barrier(0);
-        compute(k, buf_b, cb);
-        k = kn;
+        wait_k(k);
+        dec_read_k<D>(c, kb, rk);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        if (k + 8 < k1) dec_load_k<D, true>(c, k + 8, lane, kb);
+        scores(k, rk, pb);
+        wait_v(k);
+        dec_read_v<D>(vb, lane, rv);
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        if (k + 8 < k1) dec_load_v<D>(c, k + 8, vb);
+        pv(rv, pb);
+        k += 4;
     }
     __builtin_amdgcn_s_waitcnt(0);
+    lds_fence();
 
 #pragma unroll
     for (int cq = 0; cq < NQ; ++cq) {
@@ -1300,10 +1348,10 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
     int* counter = &g.counters[(bi * g.hkv + kh) * kMaxRowGroups + rg];
     if (tid == 0) {
         const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_last = (prev == n_split - 1);
+        s_last = (prev == n_split - 1);
     }
     __syncthreads();
-    if (!*s_last) return;
+    if (!s_last) return;
     for (int idx = tid; idx < n_rows * D; idx += 256) {
         const int row = row0 + idx / D, d = idx % D;
         float mm = kNegBig;
@@ -1384,13 +1432,16 @@ hipError_t run_chunk_mfma(const Geometry& g, int layer, const StreamBatch& st, i
     return hipGetLastError();
 }
 
-// At most two 16-row column blocks per block keep the accumulators and the
-// per-row softmax state in registers; larger chunks use several row groups.
+// Up to four 16-row column blocks (64 query rows) per block; larger chunks use
+// several row groups (each re-reads the window).
 template <int D>
 hipError_t run_chunk_mfma_nq(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q,
                              void* out, int n_cu, hipStream_t s) {
-    return n_q * g.group <= 16 ? run_chunk_mfma<D, 1>(g, layer, st, n_q, q, out, n_cu, s)
-                               : run_chunk_mfma<D, 2>(g, layer, st, n_q, q, out, n_cu, s);
+    const int rows = n_q * g.group;
+    static const int nq_max = env_int("A8R_DEBUG_CHUNK_NQ", 2);   // four blocks spill registers
+    return rows <= 16 || nq_max == 1 ? run_chunk_mfma<D, 1>(g, layer, st, n_q, q, out, n_cu, s)
+         : rows <= 32 || nq_max == 2 ? run_chunk_mfma<D, 2>(g, layer, st, n_q, q, out, n_cu, s)
+                                     : run_chunk_mfma<D, 4>(g, layer, st, n_q, q, out, n_cu, s);
 }
 
 bool mfma_chunk_ok(const Geometry& g, int n_q) {
