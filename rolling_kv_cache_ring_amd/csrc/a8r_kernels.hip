@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <type_traits>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -557,13 +558,13 @@ __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const De
                   sc1[0] * sl, sc1[1] * sl, sc1[2] * sl, sc1[3] * sl};
     const bool full = (k != 0) && (rho + kTile <= c.L) && (s0 + kTile <= c.W);
     if (!full) {
+        // branch-free: key index of each score, then a select
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int tt = 8 * c.gq + e;
-            int rr = rho + tt;
-            if (seam && tt < c.t_o) rr += c.W;
-            const bool ok = (rr >= 0) && (rr < c.L) && (s0 + tt < c.W);
-            if (!ok) s[e] = -INFINITY;
+            const int rr = rho + tt + ((seam & (tt < c.t_o)) ? c.W : 0);
+            const bool ok = (rr >= 0) & (rr < c.L) & (s0 + tt < c.W);
+            s[e] = ok ? s[e] : -INFINITY;
         }
     }
     float mx = s[0];
@@ -1372,6 +1373,397 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
     if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------- MFMA chunk, tiled ----
+// bf16 attention for C new positions per stream, one block per (stream, KV
+// head, split) for all C x G query rows (<= 128; row = c*G + hg): wave w owns
+// the query column blocks w, w + 4 (16 rows each) for the whole walk, so its
+// accumulators stay small and no cross-wave merge is needed.  The 4 waves walk
+// the split's visits together over a ring of NBUF block-shared visit buffers
+// (LDS DMA, each wave issuing a quarter of every visit's loads); per visit:
+//   wait for the visit's loads, barrier; refill the buffer freed by the
+//   previous visit; each wave rotates 8 of the 32 keys into a shared rotated-K
+//   tile (XOR-swizzled for the MFMA operand reads); barrier; each wave runs
+//   QK^T, the online softmax and PV for its rows.
+// Rotation: each query row is rotated once, by its own re-based index
+// r_q(c) = L - C + c; key t of a visit by R(rho + t) = R(rho) R(t), R(rho) from
+// the table row staged with the visit, R(t) held by the lane (each lane always
+// rotates the same key offset and dims).  On the first visit rho = -t_o
+// (R(t_o) conjugated), and the window's newest keys that share the oldest key's
+// tile (t < t_o, index t - t_o + W) get R(W) composed on top.  Query c sees
+// keys with index <= r_q(c): causal inside the chunk, the whole older window
+// before it.  With several splits each block writes its rows' partials
+// {m, l, O} and combine_kernel, launched next, merges them (a chip-wide merge
+// instead of one block reading every split's partials).
+template <int D>
+struct ChunkBuf {
+    static constexpr int kK = kTile * D * 2;           // raw K rows, row r at r * 2D bytes
+    static constexpr int kC = 4 * 1024;                // the R(rho) row, one copy per wave
+    static constexpr int kV = kTile * D * 2;           // V chunks, as in the decode buffers
+    static constexpr int kBytes = kK + kC + kV;
+    static constexpr int nK = 2 * (D / 32) / 4;        // DMA instructions per wave and visit
+    static constexpr int nV = (D / 16) / 4;
+    static constexpr int nI = nK + 1 + nV;
+    static constexpr int kNBuf = D == 128 ? 6 : 8;     // visit buffers (loads of NBUF - 1 visits in flight)
+};
+
+// s_waitcnt vmcnt(n * per) for n in [0, 7] (per is a compile-time count)
+template <int per>
+__device__ __forceinline__ void wait_visits(int n) {
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(per)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * per)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * per)); break;
+        case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * per)); break;
+        case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * per)); break;
+        default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * per)); break;
+    }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, StreamBatch st, int C,
+                                                      const uint16_t* __restrict__ q,
+                                                      uint16_t* __restrict__ out, int n_split) {
+    constexpr int KK = D / 32, NB = D / 16, HP = D / 64;
+    constexpr int P = D / 16;                          // rotation pairs per lane (8 lanes per key)
+    using CB = ChunkBuf<D>;
+    constexpr int NBUF = CB::kNBuf;
+    __shared__ __align__(16) unsigned char lds_buf[NBUF * CB::kBytes];
+    __shared__ __align__(16) unsigned char lds_kt[kTile * D * 2];   // rotated K of the current visit
+    __shared__ __align__(16) unsigned char lds_rw[1024];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, gq = lane >> 4;
+    const int bi = blockIdx.z, kh = blockIdx.y, split = blockIdx.x;
+    const int b = st.b0 + bi, G = g.group, W = g.window;
+    const int rows = C * G;
+
+    DecodeCtx c;
+    const int L = st.length[bi];
+    c.L = L;
+    c.W = W;
+    c.oldest = st.next_slot[bi] - L < 0 ? st.next_slot[bi] - L + W : st.next_slot[bi] - L;
+    c.rq = L - C;                      // index of the chunk's first query
+    c.n_tiles = g.w_pad / kTile;
+    c.p0t = c.oldest / kTile;
+    c.t_o = c.oldest - c.p0t * kTile;
+    c.tb0 = 8 * (n >> 2) + (n & 3);
+    c.tb1 = c.tb0 + 4;
+    c.gq = gq;
+    c.n = n;
+    c.scale_log2 = g.scale_log2;
+    c.table = g.table;
+    const int64_t pair = pair_index(g, layer, b, kh);
+    c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
+    c.vp = (const uint16_t*)g.v_ring + pair * g.w_pad * D;
+    int n_visit;
+    {
+        int last = c.oldest + L - 1;
+        if (last < W) {
+            n_visit = last / kTile - c.p0t + 1;
+        } else {
+            last -= W;
+            n_visit = c.n_tiles - c.p0t + last / kTile + 1;
+            if (n_visit > c.n_tiles) n_visit = c.n_tiles;
+        }
+    }
+    const int per = (n_visit + n_split - 1) / n_split;
+    const int k0 = split * per, k1 = min(n_visit, k0 + per);
+
+    // this wave's quarter of a visit's loads into buffer `bf`
+    auto issue = [&](int kv, int bf) {
+        unsigned char* buf = lds_buf + bf * CB::kBytes;
+        const int p = visit_tile(c, kv);
+        const int s0 = p * kTile;
+        const unsigned char* krow = (const unsigned char*)(c.kp + (int64_t)s0 * D);
+#pragma unroll
+        for (int u = 0; u < CB::nK; ++u) {
+            const int j = wave * CB::nK + u;
+            dma16(krow + j * 1024 + 16 * lane, buf + j * 1024);
+        }
+        const int rho = visit_rho(c, kv, s0);
+        dma_table_row<D>(c.table, rho < 0 ? -rho : rho, lane, buf + CB::kK + wave * 1024);
+        const uint16_t* vb = c.vp + ((int64_t)(p * 4 + gq) * D + n) * 8;
+#pragma unroll
+        for (int u = 0; u < CB::nV; ++u) {
+            const int nb = wave * CB::nV + u;
+            dma16(vb + (int64_t)nb * 16 * 8, buf + CB::kK + CB::kC + nb * 1024);
+        }
+    };
+
+    // Prologue: R(W) into LDS (wave 0), register loads (query rows, their
+    // rotation rows, the lane's R(t) pairs), then the loads of the first
+    // NBUF - 1 visits; everything before a visit's loads has landed by the
+    // time the wait for that visit returns.
+    if (wave == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
+    const int kr_t = 8 * wave + (lane >> 3);           // key offset this lane rotates
+    const int kr_i = P * (lane & 7);                   // its first pair index
+    u32x4 qr[NW][KK];
+    float4 qc[NW][HP][4];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        int row = 16 * (wave + 4 * w) + n;
+        if (row >= rows) row = 0;
+        const int cc = row / G, h = kh * G + (row - cc * G);
+        const uint16_t* qp = q + (((int64_t)bi * C + cc) * g.hq + h) * D + 8 * gq;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qr[w][kk] = *(const u32x4*)(qp + 32 * kk);
+        load_coef<D>(g.table, c.rq + cc, gq, qc[w]);
+    }
+    float2 rt[P];
+    {
+        const float2* rp = g.table + (int64_t)kr_t * (D / 2) + kr_i;
+#pragma unroll
+        for (int i = 0; i < P; ++i) rt[i] = rp[i];
+    }
+    for (int i = 0; i < NBUF - 1; ++i)
+        if (k0 + i < k1) issue(k0 + i, i);
+
+    // queries rotated once into MFMA B operands (zero for padding rows)
+    bf16x8 qb[NW][KK];
+    int rq_col[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int row = 16 * (wave + 4 * w) + n;
+        rotate_row<D>(qc[w], qr[w], qb[w]);
+        if (row >= rows) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qb[w][kk][e] = (__bf16)0.f;
+        }
+        rq_col[w] = row < rows ? c.rq + row / G : -1;
+    }
+    // column blocks with at least one real row (wave-uniform)
+    const bool act0 = 16 * wave < rows, act1 = NW > 1 && 16 * (wave + 4) < rows;
+
+    floatx4 o[NW][NB];
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) o[w][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m[NW], l[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        m[w] = kNegBig;
+        l[w] = 0.f;
+    }
+    const int r_last = L - 1;
+
+    // One visit with buffer index BF known at compile time (so every LDS
+    // address is a constant offset into lds_buf); the walk runs the steps
+    // 0 .. NBUF-1 in turn.
+    auto step = [&](auto bfc, int kv) {
+        constexpr int bf = decltype(bfc)::value;
+        unsigned char* buf = lds_buf + bf * CB::kBytes;
+        // this wave's loads of visit kv have landed once at most the loads of
+        // the visits after it (up to NBUF - 2 of them) are outstanding
+        wait_visits<CB::nI>(min(NBUF - 2, k1 - 1 - kv));
+        __builtin_amdgcn_s_barrier();          // ... and every wave's; visit kv - 1 is done everywhere
+        __builtin_amdgcn_sched_barrier(0);
+        lds_fence();
+        if (kv + NBUF - 1 < k1) issue(kv + NBUF - 1, (bf + NBUF - 1) % NBUF);
+
+        // rotate key kr_t (pairs kr_i .. kr_i + P - 1) into the shared tile
+        const int p = visit_tile(c, kv);
+        const int s0 = p * kTile;
+        const int rho = visit_rho(c, kv, s0);
+        const bool seam = (kv == 0) && (c.t_o > 0);
+        {
+            // R(rho) pairs kr_i .. as P/2 float4 (16-byte LDS reads)
+            const float4* br = (const float4*)(buf + CB::kK + wave * 1024) + kr_i / 2;
+            const unsigned char* kraw = buf + kr_t * D * 2;
+            float2 cf[P];
+#pragma unroll
+            for (int i2 = 0; i2 < P / 2; ++i2) {
+                const float4 b4 = br[i2];
+                float2 bs[2] = {float2{b4.x, b4.y}, float2{b4.z, b4.w}};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int i = 2 * i2 + h;
+                    if (kv == 0) bs[h].y = -bs[h].y;                    // R(-t_o)
+                    cf[i] = float2{bs[h].x * rt[i].x - bs[h].y * rt[i].y, bs[h].y * rt[i].x + bs[h].x * rt[i].y};
+                }
+            }
+            if (seam && kr_t < c.t_o) {                            // index kr_t - t_o + W
+                const float4* wr = (const float4*)lds_rw + kr_i / 2;
+#pragma unroll
+                for (int i2 = 0; i2 < P / 2; ++i2) {
+                    const float4 w4 = wr[i2];
+                    const float2 w2[2] = {float2{w4.x, w4.y}, float2{w4.z, w4.w}};
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int i = 2 * i2 + h;
+                        const float2 a = cf[i];
+                        cf[i] = float2{w2[h].x * a.x - w2[h].y * a.y, w2[h].y * a.x + w2[h].x * a.y};
+                    }
+                }
+            }
+            uint32_t x1w[P / 2], x2w[P / 2];
+            if constexpr (P == 8) {
+                const u32x4 a1 = *(const u32x4*)(kraw + 2 * kr_i), a2 = *(const u32x4*)(kraw + 2 * (kr_i + D / 2));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x1w[i] = a1[i];
+                    x2w[i] = a2[i];
+                }
+            } else {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 a1 = *(const u32x2*)(kraw + 2 * kr_i), a2 = *(const u32x2*)(kraw + 2 * (kr_i + D / 2));
+                x1w[0] = a1[0];
+                x1w[1] = a1[1];
+                x2w[0] = a2[0];
+                x2w[1] = a2[1];
+            }
+            __bf16 y1[P], y2[P];
+#pragma unroll
+            for (int i = 0; i < P; ++i) {
+                const float x1 = (i & 1) ? hi_bf16(x1w[i >> 1]) : lo_bf16(x1w[i >> 1]);
+                const float x2 = (i & 1) ? hi_bf16(x2w[i >> 1]) : lo_bf16(x2w[i >> 1]);
+                y1[i] = (__bf16)(x1 * cf[i].x - x2 * cf[i].y);
+                y2[i] = (__bf16)(x2 * cf[i].x + x1 * cf[i].y);
+            }
+            // dims kr_i .. (16-byte column kr_i / 8) and + D/2 (column + D/16)
+            unsigned char* d1 = lds_kt + 16 * k_pos<D>(kr_t, kr_i / 8) + 2 * (kr_i % 8);
+            unsigned char* d2 = lds_kt + 16 * k_pos<D>(kr_t, (kr_i + D / 2) / 8) + 2 * (kr_i % 8);
+            if constexpr (P == 8) {
+                bf16x8 v1, v2;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    v1[i] = y1[i];
+                    v2[i] = y2[i];
+                }
+                *(bf16x8*)d1 = v1;
+                *(bf16x8*)d2 = v2;
+            } else {
+                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                bf16x4 v1, v2;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v1[i] = y1[i];
+                    v2[i] = y2[i];
+                }
+                *(bf16x4*)d1 = v1;
+                *(bf16x4*)d2 = v2;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_s_barrier();          // rotated tile complete
+        __builtin_amdgcn_sched_barrier(0);
+        lds_fence();
+
+        if (!act0) return;                     // a wave without query rows only helps with the tile
+        bf16x8 kA[2][KK];
+        {
+            const u32x4* kt = (const u32x4*)lds_kt;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                kA[0][kk] = __builtin_bit_cast(bf16x8, kt[k_pos<D>(c.tb0, gq + 4 * kk)]);
+                kA[1][kk] = __builtin_bit_cast(bf16x8, kt[k_pos<D>(c.tb1, gq + 4 * kk)]);
+            }
+        }
+        u32x4 vv[NB];
+        {
+            const u32x4* lb = (const u32x4*)(buf + CB::kK + CB::kC) + lane;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) vv[nb] = lb[nb * 64];
+        }
+        const bool full = (kv != 0) && (rho + kTile <= c.rq + 1) && (s0 + kTile <= W);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            if (w == 1 && !act1) break;
+            floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[0][kk], qb[w][kk], a0, 0, 0, 0);
+                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[1][kk], qb[w][kk], a1, 0, 0, 0);
+            }
+            float s[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] *= c.scale_log2;
+            if (!full) {
+                // branch-free: key index r of each score, then a select
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tt = 8 * gq + e;
+                    const int r = rho + tt + ((seam & (tt < c.t_o)) ? W : 0);
+                    const bool ok = (r >= 0) & (r <= r_last) & ((rq_col[w] < 0) | (r <= rq_col[w])) & (s0 + tt < W);
+                    s[e] = ok ? s[e] : -INFINITY;
+                }
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (mx > m[w] + 8.f) {
+                const float alpha = exp2f(m[w] - mx);
+                l[w] *= alpha;
+#pragma unroll
+                for (int i = 0; i < NB; ++i) o[w][i] *= alpha;
+                m[w] = mx;
+            }
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe = exp2f(s[e] - m[w]);
+                l[w] += pe;
+                pb[e] = (__bf16)pe;
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                o[w][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv[nb]), pb, o[w][nb],
+                                                                   0, 0, 0);
+        }
+    };
+    using std::integral_constant;
+    for (int kv = k0; kv < k1; kv += NBUF) {
+        step(integral_constant<int, 0>{}, kv);
+        if (kv + 1 < k1) step(integral_constant<int, 1>{}, kv + 1);
+        if (kv + 2 < k1) step(integral_constant<int, 2>{}, kv + 2);
+        if (kv + 3 < k1) step(integral_constant<int, 3>{}, kv + 3);
+        if (kv + 4 < k1) step(integral_constant<int, 4>{}, kv + 4);
+        if (kv + 5 < k1) step(integral_constant<int, 5>{}, kv + 5);
+        if constexpr (NBUF > 6) {
+            if (kv + 6 < k1) step(integral_constant<int, (NBUF > 6 ? 6 : 0)>{}, kv + 6);
+            if (kv + 7 < k1) step(integral_constant<int, (NBUF > 7 ? 7 : 0)>{}, kv + 7);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // this block's partial for the wave's rows: O^T element (dim 16 nb + 4 gq + j,
+    // column n) in o[w][nb][j]
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        l[w] += __shfl_xor(l[w], 16);
+        l[w] += __shfl_xor(l[w], 32);
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int row = 16 * (wave + 4 * w) + n;
+        if (row >= rows) continue;
+        const int cc = row / G, h = kh * G + (row - cc * G);
+        if (n_split == 1) {
+            const float inv = 1.f / l[w];
+            uint16_t* op = out + (((int64_t)bi * C + cc) * g.hq + h) * D;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) op[16 * nb + 4 * gq + j] = f32_to_bf16_bits(o[w][nb][j] * inv);
+        } else {
+            // partials for combine_kernel (launched next on the same stream)
+            const int64_t pr = part_row(g, bi, kh, split, row);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                *(float4*)&g.part_o[pr * D + 16 * nb + 4 * gq] =
+                    float4{o[w][nb][0], o[w][nb][1], o[w][nb][2], o[w][nb][3]};
+            if (gq == 0) *(float2*)&g.part_ml[pr * 2] = float2{m[w], l[w]};
+        }
+    }
+}
+
 int env_int(const char* name, int dflt) {
     const char* s = getenv(name);
     return s ? atoi(s) : dflt;
@@ -1444,6 +1836,20 @@ hipError_t run_chunk_mfma_nq(const Geometry& g, int layer, const StreamBatch& st
                                      : run_chunk_mfma<D, 4>(g, layer, st, n_q, q, out, n_cu, s);
 }
 
+template <int D, int NW>
+hipError_t run_chunk_tiled(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q, void* out,
+                           int n_cu, hipStream_t s) {
+    static const int target = env_int("A8R_DEBUG_CHUNK_BLOCKS", 0);
+    const int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, target > 0 ? target : n_cu, 4);
+    hipLaunchKernelGGL((chunk_tiled<D, NW>), dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st, n_q,
+                       (const uint16_t*)q, (uint16_t*)out, n_split);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_split == 1) return e;
+    // the splits' partials are merged by a second, chip-wide kernel
+    hipLaunchKernelGGL((combine_kernel<D, 2>), dim3(st.nb * n_q * g.hq), dim3(D), 0, s, g, n_q, n_split, out);
+    return hipGetLastError();
+}
+
 bool mfma_chunk_ok(const Geometry& g, int n_q) {
     return g.elem_bytes == 2 && (g.d == 64 || g.d == 128) && n_q >= 2 && n_q <= kMaxPartialQ &&
            n_q * g.group <= 32 * kMaxRowGroups;
@@ -1474,6 +1880,15 @@ hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now
     if (allow_mfma && n_q == 1 && mfma_decode_ok(g))
         return g.d == 128 ? run_decode_mfma<128>(g, layer, now, q, out, n_cu, nullptr, nullptr, s)
                           : run_decode_mfma<64>(g, layer, now, q, out, n_cu, nullptr, nullptr, s);
+    static const int tiled = env_int("A8R_DEBUG_CHUNK_TILED", 1);
+    if (allow_mfma && mfma_chunk_ok(g, n_q) && tiled) {
+        const bool one = n_q * g.group <= 64;
+        if (g.d == 128)
+            return one ? run_chunk_tiled<128, 1>(g, layer, now, n_q, q, out, n_cu, s)
+                       : run_chunk_tiled<128, 2>(g, layer, now, n_q, q, out, n_cu, s);
+        return one ? run_chunk_tiled<64, 1>(g, layer, now, n_q, q, out, n_cu, s)
+                   : run_chunk_tiled<64, 2>(g, layer, now, n_q, q, out, n_cu, s);
+    }
     if (allow_mfma && mfma_chunk_ok(g, n_q))
         return g.d == 128 ? run_chunk_mfma_nq<128>(g, layer, now, n_q, q, out, n_cu, s)
                           : run_chunk_mfma_nq<64>(g, layer, now, n_q, q, out, n_cu, s);
