@@ -42,6 +42,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegBig = -1.0e30f;   // running-max seed: exp2(x - kNegBig) never NaNs
 
+// 2^x as the single hardware instruction (v_exp_f32): arguments here are <= 8,
+// and results below 2^-126 flush to 0, which is harmless for softmax weights.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -156,14 +160,31 @@ __global__ __launch_bounds__(128) void combine_kernel(Geometry g, int n_q, int n
     const int bi = o / (g.hq * n_q);
     const int kh = h / g.group, row = c * g.group + (h - kh * g.group);
     const int d = threadIdx.x;
+    // every split's loads are issued together (one round trip), then combined
+    // in split order
+    float mv[kMaxSplits], lv[kMaxSplits], ov[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        if (s < n_split) {
+            const int64_t pr = part_row(g, bi, kh, s, row);
+            const float2 ml = *(const float2*)&g.part_ml[pr * 2];
+            mv[s] = ml.x;
+            lv[s] = ml.y;
+            ov[s] = g.part_o[pr * D + d];
+        }
+    }
     float mmax = kNegBig;
-    for (int s = 0; s < n_split; ++s) mmax = fmaxf(mmax, g.part_ml[part_row(g, bi, kh, s, row) * 2]);
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+        if (s < n_split) mmax = fmaxf(mmax, mv[s]);
     float num = 0.f, den = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-        const int64_t pr = part_row(g, bi, kh, s, row);
-        const float w = exp2f(g.part_ml[pr * 2] - mmax);
-        den += w * g.part_ml[pr * 2 + 1];
-        num += w * g.part_o[pr * D + d];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        if (s < n_split) {
+            const float w = exp2f(mv[s] - mmax);
+            den += w * lv[s];
+            num += w * ov[s];
+        }
     }
     store_elem<EB>(out, (((int64_t)bi * n_q + c) * g.hq + h) * D + d, num / den);
 }
@@ -572,18 +593,22 @@ __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const De
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // lazy rescale: keep the running max unless a score exceeds it by 2^8
-    if (mx > m + 8.f) {
-        const float alpha = exp2f(m - mx);
+    // lazy rescale: keep the running max unless a score exceeds it by 2^8; the
+    // branch is taken by the whole wave when any column needs it (the others
+    // multiply by exactly 1)
+    const bool grow = mx > m + 8.f;
+    if (__any(grow)) {
+        const float mn = grow ? mx : m;
+        const float alpha = fast_exp2(m - mn);
         l *= alpha;
 #pragma unroll
         for (int i = 0; i < NB; ++i) o[i] *= alpha;
-        m = mx;
+        m = mn;
     }
     bf16x8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float pe = exp2f(s[e] - m);
+        const float pe = fast_exp2(s[e] - m);
         l += pe;
         pb[e] = (__bf16)pe;
     }
@@ -1403,7 +1428,9 @@ struct ChunkBuf {
     static constexpr int nK = 2 * (D / 32) / 4;        // DMA instructions per wave and visit
     static constexpr int nV = (D / 16) / 4;
     static constexpr int nI = nK + 1 + nV;
-    static constexpr int kNBuf = D == 128 ? 6 : 8;     // visit buffers (loads of NBUF - 1 visits in flight)
+    // visit buffers per wave group (loads of NBUF - 1 of the group's visits in flight)
+    template <int WG>
+    static constexpr int nbuf() { return WG == 1 ? (D == 128 ? 6 : 8) : (D == 128 ? 3 : 4); }
 };
 
 // s_waitcnt vmcnt(n * per) for n in [0, 7] (per is a compile-time count)
@@ -1421,20 +1448,23 @@ __device__ __forceinline__ void wait_visits(int n) {
     }
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, StreamBatch st, int C,
+template <int D, int NW, int WG>
+__global__ __launch_bounds__(256 * WG, 1) void chunk_tiled(Geometry g, int layer, StreamBatch st, int C,
                                                       const uint16_t* __restrict__ q,
                                                       uint16_t* __restrict__ out, int n_split) {
     constexpr int KK = D / 32, NB = D / 16, HP = D / 64;
     constexpr int P = D / 16;                          // rotation pairs per lane (8 lanes per key)
     using CB = ChunkBuf<D>;
-    constexpr int NBUF = CB::kNBuf;
-    __shared__ __align__(16) unsigned char lds_buf[NBUF * CB::kBytes];
-    __shared__ __align__(16) unsigned char lds_kt[kTile * D * 2];   // rotated K of the current visit
+    constexpr int NBUF = CB::template nbuf<WG>();
+    __shared__ __align__(16) unsigned char lds_bufs[WG * NBUF * CB::kBytes];
+    __shared__ __align__(16) unsigned char lds_kts[WG * kTile * D * 2];   // rotated K of each group's visit
     __shared__ __align__(16) unsigned char lds_rw[1024];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_b = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wg = wave_b >> 2, wave = wave_b & 3;      // wave group, wave within the group
+    unsigned char* lds_buf = lds_bufs + wg * NBUF * CB::kBytes;
+    unsigned char* lds_kt = lds_kts + wg * kTile * D * 2;
     const int n = lane & 15, gq = lane >> 4;
     const int bi = blockIdx.z, kh = blockIdx.y, split = blockIdx.x;
     const int b = st.b0 + bi, G = g.group, W = g.window;
@@ -1497,7 +1527,7 @@ __global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, Str
     // rotation rows, the lane's R(t) pairs), then the loads of the first
     // NBUF - 1 visits; everything before a visit's loads has landed by the
     // time the wait for that visit returns.
-    if (wave == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
+    if (wave_b == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
     const int kr_t = 8 * wave + (lane >> 3);           // key offset this lane rotates
     const int kr_i = P * (lane & 7);                   // its first pair index
     u32x4 qr[NW][KK];
@@ -1518,8 +1548,12 @@ __global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, Str
 #pragma unroll
         for (int i = 0; i < P; ++i) rt[i] = rp[i];
     }
+    // group wg walks visits k0 + wg, k0 + wg + WG, ... (n_mine of them); all
+    // waves run n_steps steps (two block-wide barriers each)
+    const int n_steps = (k1 - k0 + WG - 1) / WG;
+    const int n_mine = k0 + wg < k1 ? (k1 - k0 - wg + WG - 1) / WG : 0;
     for (int i = 0; i < NBUF - 1; ++i)
-        if (k0 + i < k1) issue(k0 + i, i);
+        if (i < n_mine) issue(k0 + wg + WG * i, i);
 
     // queries rotated once into MFMA B operands (zero for padding rows)
     bf16x8 qb[NW][KK];
@@ -1555,23 +1589,25 @@ __global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, Str
     // One visit with buffer index BF known at compile time (so every LDS
     // address is a constant offset into lds_buf); the walk runs the steps
     // 0 .. NBUF-1 in turn.
-    auto step = [&](auto bfc, int kv) {
+    auto step = [&](auto bfc, int si) {
         constexpr int bf = decltype(bfc)::value;
         unsigned char* buf = lds_buf + bf * CB::kBytes;
-        // this wave's loads of visit kv have landed once at most the loads of
-        // the visits after it (up to NBUF - 2 of them) are outstanding
-        wait_visits<CB::nI>(min(NBUF - 2, k1 - 1 - kv));
-        __builtin_amdgcn_s_barrier();          // ... and every wave's; visit kv - 1 is done everywhere
+        const int kv = k0 + wg + WG * si;       // this group's visit (if si < n_mine)
+        const bool mine = si < n_mine;
+        // this wave's loads of the visit have landed once at most the loads of
+        // the group's visits after it (up to NBUF - 2 of them) are outstanding
+        if (mine) wait_visits<CB::nI>(min(NBUF - 2, n_mine - 1 - si));
+        __builtin_amdgcn_s_barrier();          // ... and every wave's; the previous step is done everywhere
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
-        if (kv + NBUF - 1 < k1) issue(kv + NBUF - 1, (bf + NBUF - 1) % NBUF);
+        if (si + NBUF - 1 < n_mine) issue(kv + WG * (NBUF - 1), (bf + NBUF - 1) % NBUF);
 
         // rotate key kr_t (pairs kr_i .. kr_i + P - 1) into the shared tile
         const int p = visit_tile(c, kv);
         const int s0 = p * kTile;
         const int rho = visit_rho(c, kv, s0);
         const bool seam = (kv == 0) && (c.t_o > 0);
-        {
+        if (mine) {
             // R(rho) pairs kr_i .. as P/2 float4 (16-byte LDS reads)
             const float4* br = (const float4*)(buf + CB::kK + wave * 1024) + kr_i / 2;
             const unsigned char* kraw = buf + kr_t * D * 2;
@@ -1587,7 +1623,8 @@ __global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, Str
                     cf[i] = float2{bs[h].x * rt[i].x - bs[h].y * rt[i].y, bs[h].y * rt[i].x + bs[h].x * rt[i].y};
                 }
             }
-            if (seam && kr_t < c.t_o) {                            // index kr_t - t_o + W
+            if (seam) {                                    // first visit only (wave-uniform)
+                const bool wrap = kr_t < c.t_o;            // index kr_t - t_o + W: R(W) on top
                 const float4* wr = (const float4*)lds_rw + kr_i / 2;
 #pragma unroll
                 for (int i2 = 0; i2 < P / 2; ++i2) {
@@ -1597,7 +1634,8 @@ __global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, Str
                     for (int h = 0; h < 2; ++h) {
                         const int i = 2 * i2 + h;
                         const float2 a = cf[i];
-                        cf[i] = float2{w2[h].x * a.x - w2[h].y * a.y, w2[h].y * a.x + w2[h].x * a.y};
+                        const float2 r = {w2[h].x * a.x - w2[h].y * a.y, w2[h].y * a.x + w2[h].x * a.y};
+                        cf[i] = wrap ? r : a;
                     }
                 }
             }
@@ -1654,7 +1692,7 @@ __global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, Str
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
 
-        if (!act0) return;                     // a wave without query rows only helps with the tile
+        if (!act0 || !mine) return;            // a wave without query rows only helps with the tile
         bf16x8 kA[2][KK];
         {
             const u32x4* kt = (const u32x4*)lds_kt;
@@ -1698,17 +1736,19 @@ __global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, Str
             for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            if (mx > m[w] + 8.f) {
-                const float alpha = exp2f(m[w] - mx);
+            const bool grow = mx > m[w] + 8.f;           // lazy rescale, wave-uniform branch
+            if (__any(grow)) {
+                const float mn = grow ? mx : m[w];
+                const float alpha = fast_exp2(m[w] - mn);
                 l[w] *= alpha;
 #pragma unroll
                 for (int i = 0; i < NB; ++i) o[w][i] *= alpha;
-                m[w] = mx;
+                m[w] = mn;
             }
             bf16x8 pb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pe = exp2f(s[e] - m[w]);
+                const float pe = fast_exp2(s[e] - m[w]);
                 l[w] += pe;
                 pb[e] = (__bf16)pe;
             }
@@ -1719,16 +1759,20 @@ __global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, Str
         }
     };
     using std::integral_constant;
-    for (int kv = k0; kv < k1; kv += NBUF) {
-        step(integral_constant<int, 0>{}, kv);
-        if (kv + 1 < k1) step(integral_constant<int, 1>{}, kv + 1);
-        if (kv + 2 < k1) step(integral_constant<int, 2>{}, kv + 2);
-        if (kv + 3 < k1) step(integral_constant<int, 3>{}, kv + 3);
-        if (kv + 4 < k1) step(integral_constant<int, 4>{}, kv + 4);
-        if (kv + 5 < k1) step(integral_constant<int, 5>{}, kv + 5);
+    for (int si = 0; si < n_steps; si += NBUF) {
+        step(integral_constant<int, 0>{}, si);
+        if (si + 1 < n_steps) step(integral_constant<int, (NBUF > 1 ? 1 : 0)>{}, si + 1);
+        if (si + 2 < n_steps) step(integral_constant<int, (NBUF > 2 ? 2 : 0)>{}, si + 2);
+        if constexpr (NBUF > 3) {
+            if (si + 3 < n_steps) step(integral_constant<int, (NBUF > 3 ? 3 : 0)>{}, si + 3);
+        }
+        if constexpr (NBUF > 4) {
+            if (si + 4 < n_steps) step(integral_constant<int, (NBUF > 4 ? 4 : 0)>{}, si + 4);
+            if (si + 5 < n_steps) step(integral_constant<int, (NBUF > 5 ? 5 : 0)>{}, si + 5);
+        }
         if constexpr (NBUF > 6) {
-            if (kv + 6 < k1) step(integral_constant<int, (NBUF > 6 ? 6 : 0)>{}, kv + 6);
-            if (kv + 7 < k1) step(integral_constant<int, (NBUF > 7 ? 7 : 0)>{}, kv + 7);
+            if (si + 6 < n_steps) step(integral_constant<int, (NBUF > 6 ? 6 : 0)>{}, si + 6);
+            if (si + 7 < n_steps) step(integral_constant<int, (NBUF > 7 ? 7 : 0)>{}, si + 7);
         }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -1739,6 +1783,41 @@ __global__ __launch_bounds__(256, 1) void chunk_tiled(Geometry g, int layer, Str
     for (int w = 0; w < NW; ++w) {
         l[w] += __shfl_xor(l[w], 16);
         l[w] += __shfl_xor(l[w], 32);
+    }
+    if constexpr (WG == 2) {
+        // group 1 hands its (m, l, O) of every row to group 0 through LDS
+        float* xo = (float*)lds_bufs;                         // [row][D]
+        float* xml = xo + 4 * NW * 16 * D;                    // [row][2]
+        __syncthreads();
+        if (wg == 1) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int lr = 16 * (wave + 4 * w) + n;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    *(float4*)&xo[lr * D + 16 * nb + 4 * gq] = float4{o[w][nb][0], o[w][nb][1], o[w][nb][2], o[w][nb][3]};
+                if (gq == 0) *(float2*)&xml[lr * 2] = float2{m[w], l[w]};
+            }
+        }
+        __syncthreads();
+        if (wg == 1) return;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int lr = 16 * (wave + 4 * w) + n;
+            const float2 ml1 = *(const float2*)&xml[lr * 2];
+            const float mn = fmaxf(m[w], ml1.x);
+            const float a0 = exp2f(m[w] - mn), a1 = exp2f(ml1.x - mn);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float4 x = *(const float4*)&xo[lr * D + 16 * nb + 4 * gq];
+                o[w][nb][0] = o[w][nb][0] * a0 + x.x * a1;
+                o[w][nb][1] = o[w][nb][1] * a0 + x.y * a1;
+                o[w][nb][2] = o[w][nb][2] * a0 + x.z * a1;
+                o[w][nb][3] = o[w][nb][3] * a0 + x.w * a1;
+            }
+            l[w] = l[w] * a0 + ml1.y * a1;
+            m[w] = mn;
+        }
     }
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -1840,9 +1919,15 @@ template <int D, int NW>
 hipError_t run_chunk_tiled(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q, void* out,
                            int n_cu, hipStream_t s) {
     static const int target = env_int("A8R_DEBUG_CHUNK_BLOCKS", 0);
+    static const int groups = env_int("A8R_DEBUG_CHUNK_GROUPS", 2);
     const int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, target > 0 ? target : n_cu, 4);
-    hipLaunchKernelGGL((chunk_tiled<D, NW>), dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st, n_q,
-                       (const uint16_t*)q, (uint16_t*)out, n_split);
+    // two wave groups (two waves per SIMD) where the registers allow it
+    if (groups == 2)
+        hipLaunchKernelGGL((chunk_tiled<D, NW, 2>), dim3(n_split, g.hkv, st.nb), dim3(512), 0, s, g, layer, st,
+                           n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
+    else
+        hipLaunchKernelGGL((chunk_tiled<D, NW, 1>), dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st,
+                           n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split == 1) return e;
     // the splits' partials are merged by a second, chip-wide kernel
