@@ -115,7 +115,7 @@ struct Ledger {
 };
 
 struct Layout {
-    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, counter_off, part_t_off, total;
+    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, counter_off, part_t_off, part_x_off, total;
     int w_pad, rows_max;
 };
 
@@ -179,6 +179,10 @@ a8r_status compute_layout(const a8r_config* c, Layout* lay) {
     lay->part_t_off = off;
     off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kMaxSplits * a8r::kMaxGroupTagged *
                                   (c->head_dim + 2) * sizeof(uint64_t),
+                        a8r::kAlign);
+    lay->part_x_off = off;
+    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kMaxGroupTagged * c->head_dim *
+                                  sizeof(uint64_t),
                         a8r::kAlign);
     lay->total = off;
     lay->w_pad = w_pad;
@@ -313,6 +317,7 @@ a8r_status a8r_cache_create(const a8r_config* cfg, void* hip_stream, void* works
     g.part_ml = (float*)(b + lay.part_ml_off);
     g.counters = (int*)(b + lay.counter_off);
     g.part_t = (uint64_t*)(b + lay.part_t_off);
+    g.part_x = (uint64_t*)(b + lay.part_x_off);
     g.n_layers = cfg->n_layers;
     g.n_streams = cfg->n_streams;
     g.hq = cfg->n_q_heads;
@@ -328,6 +333,8 @@ a8r_status a8r_cache_create(const a8r_config* cfg, void* hip_stream, void* works
 
     const std::vector<float> table = build_table(cfg->window, cfg->head_dim, cfg->rope_theta);
     e = hipMemsetAsync(c->base, 0, lay.total, c->stream);
+    if (e == hipSuccess)   // every exchange slot starts empty (all ones)
+        e = hipMemsetAsync(b + lay.part_x_off, 0xff, lay.total - lay.part_x_off, c->stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(b + lay.table_off, table.data(), table.size() * sizeof(float), hipMemcpyHostToDevice,
                            c->stream);

@@ -33,7 +33,8 @@ constexpr int kMaxPartialQ = 16;   // chunk sizes above this run without splits
 constexpr size_t kAlign = 256;
 constexpr int kBatch = 128;        // streams per launch (their state travels in the arguments)
 constexpr int kMaxRowGroups = 4;   // query row groups of one KV head in the chunk kernel
-constexpr int kMaxGroupTagged = 16; // query heads per KV head in the MFMA decode kernel
+constexpr int kMaxGroupTagged = 16;   // query heads per KV head in the MFMA decode kernel
+constexpr uint64_t kSlotEmpty = ~(uint64_t)0;   // an exchange slot holding no partial
 
 struct DevState {
     int64_t next_pos;   // absolute position of the next token
@@ -62,6 +63,8 @@ struct Geometry {
     int* counters;      // [n_streams][n_kv_heads][kMaxRowGroups] split arrival counters, 0 between calls
     uint64_t* part_t;   // decode split partials tagged with the launch epoch (high word):
                         // [n_streams][n_kv_heads][kMaxSplits][kMaxGroupTagged][D + 2] (O..., m, l)
+    uint64_t* part_x;   // two-split decode exchange slots, one per output element:
+                        // [n_streams][n_kv_heads][kMaxGroupTagged][D], kSlotEmpty between calls
     int n_layers, n_streams, hq, hkv, group, d, window, w_pad;
     int elem_bytes;     // 2 (bf16) or 4 (f32)
     int rows_max;       // max(1, min(max_chunk, kMaxPartialQ)) * group

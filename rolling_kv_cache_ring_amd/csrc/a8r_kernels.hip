@@ -865,65 +865,125 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         g.state[(int64_t)layer * g.n_streams + b] = ns;
     }
 
+    // Across the block's 4 waves: each wave rescales its {l, O} to the block's
+    // running max before writing them, so that the per-element merge is a sum.
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    if (n < G && gq == 0) red_ml[wave][n][0] = m;
     __syncthreads();
-    if (n < G) {
-        if (gq == 0) {
-            red_ml[wave][n][0] = m;
-            red_ml[wave][n][1] = l;
+    {
+        const int hn = n < G ? n : 0;
+        float mb = red_ml[0][hn][0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) mb = fmaxf(mb, red_ml[w][hn][0]);
+        const float f = fast_exp2(m - mb);
+        if (n < G) {
+            if (gq == 0) red_ml[wave][n][1] = l * f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) red_o[wave][n][16 * nb + 4 * gq + j] = o[nb][j] * f;
         }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) red_o[wave][n][16 * nb + 4 * gq + j] = o[nb][j];
     }
     __syncthreads();
 
     // The block's partial {m, l, O} for each (head, dim) this thread owns.
-    // Splits publish partials as (value, epoch) pairs with single 64-bit
+    //
+    // Two splits (the usual case) meet per output element in an exchange slot
+    // that holds kSlotEmpty between calls: each swaps in its normalized partial
+    // (O / l, m + log2 l) with one 64-bit atomic exchange.  The one that gets the
+    // other's partial back (it came second) merges the element, writes the
+    // output and empties the slot; the one that gets kSlotEmpty back is done.
+    // One round trip, no block-wide count.
+    //
+    // More splits publish partials as (value, epoch) pairs with single 64-bit
     // agent-coherent stores and count themselves in right away; the last block
     // to arrive merges, re-reading any element whose tag is not yet this
-    // launch's (the stores are already in flight, so the wait is bounded).  The
-    // merge sums the splits in index order whichever block does it, so results
-    // are the same run to run.
+    // launch's (the stores are already in flight, so the wait is bounded).
+    //
+    // Either way the merge combines the splits in index order whichever block
+    // does it, so results are the same run to run.
     constexpr int kPer = (kMaxGroupTagged * D + 255) / 256;
     float p_num[kPer], p_den[kPer], p_m[kPer];
+    uint64_t x_mine[kPer], x_old[kPer];
     const uint32_t epoch = st.epoch;
     auto tagged = [&](float x) { return ((uint64_t)epoch << 32) | __float_as_uint(x); };
     auto trow = [&](int sp, int h) {
         return g.part_t + ((((int64_t)bi * g.hkv + kh) * kMaxSplits + sp) * kMaxGroupTagged + h) * (D + 2);
     };
+    // elements of this thread: the same count across a wave (G * D is a
+    // multiple of 64), so the loops below branch uniformly
+    const int n_mine = __builtin_amdgcn_readfirstlane((G * D - 64 * wave + 255) / 256);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
+        if (i >= n_mine) break;
         const int idx = tid + 256 * i;
-        if (idx >= G * D) break;
         const int h = idx / D, d = idx - h * D;
-        float mm = red_ml[0][h][0];
+        float mm = red_ml[0][h][0], num = red_o[0][h][d], den = red_ml[0][h][1];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) mm = fmaxf(mm, red_ml[w][h][0]);
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float f = exp2f(red_ml[w][h][0] - mm);
-            num += f * red_o[w][h][d];
-            den += f * red_ml[w][h][1];
+        for (int w = 1; w < 4; ++w) {
+            mm = fmaxf(mm, red_ml[w][h][0]);
+            num += red_o[w][h][d];
+            den += red_ml[w][h][1];
         }
         p_num[i] = num;
         p_den[i] = den;
         p_m[i] = mm;
-        if (n_split == 1) {
-            out[((int64_t)bi * g.hq + kh * G + h) * D + d] = f32_to_bf16_bits(num / den);
-        } else {
-            uint64_t* pr = trow(split, h);
-            __hip_atomic_store(pr + d, tagged(num), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (d == 0) {
-                __hip_atomic_store(pr + D, tagged(mm), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(pr + D + 1, tagged(den), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    auto out_at = [&](int idx) -> uint16_t& { return out[((int64_t)bi * g.hq + kh * G) * D + idx]; };
+    if (n_split == 1) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            if (i >= n_mine) break;
+            out_at(tid + 256 * i) = f32_to_bf16_bits(p_num[i] / p_den[i]);
+        }
+        return;
+    }
+    if (n_split == 2) {
+        uint64_t* slots = g.part_x + ((int64_t)bi * g.hkv + kh) * kMaxGroupTagged * D;
+        // every exchange issued before any result is needed
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            if (i >= n_mine) break;
+            // an empty split (short window) has den = 0: weight 0 in the merge
+            const bool live = p_den[i] > 0.f;             // then den >= 1 (the max term is 1)
+            const float on = live ? p_num[i] * __builtin_amdgcn_rcpf(p_den[i]) : 0.f;
+            uint32_t lse = __float_as_uint(live ? p_m[i] + __builtin_amdgcn_logf(p_den[i]) : -INFINITY);
+            if (lse == 0xffffffffu) lse = 0x7fc00000u;          // never kSlotEmpty
+            x_mine[i] = ((uint64_t)lse << 32) | __float_as_uint(on);
+            x_old[i] = __hip_atomic_exchange(slots + tid + 256 * i, x_mine[i], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            if (i >= n_mine) break;
+            const uint64_t other = x_old[i];
+            const bool second = other != kSlotEmpty;          // else the other split merges it
+            const uint64_t a = split == 0 ? x_mine[i] : other, c1 = split == 0 ? other : x_mine[i];
+            const float la = __uint_as_float((uint32_t)(a >> 32)), lb = __uint_as_float((uint32_t)(c1 >> 32));
+            const float mx = fmaxf(la, lb);
+            const float wa = fast_exp2(la - mx), wb = fast_exp2(lb - mx);
+            const float r = (__uint_as_float((uint32_t)a) * wa + __uint_as_float((uint32_t)c1) * wb) *
+                            __builtin_amdgcn_rcpf(wa + wb);
+            if (second) {
+                out_at(tid + 256 * i) = f32_to_bf16_bits(r);
+                __hip_atomic_store(slots + tid + 256 * i, kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        return;
     }
-    if (n_split == 1) return;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        if (i >= n_mine) break;
+        const int idx = tid + 256 * i;
+        const int h = idx / D, d = idx - h * D;
+        uint64_t* pr = trow(split, h);
+        __hip_atomic_store(pr + d, tagged(p_num[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) {
+            __hip_atomic_store(pr + D, tagged(p_m[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pr + D + 1, tagged(p_den[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 
     __syncthreads();            // every store of the block has been issued
     int* counter = &g.counters[(bi * g.hkv + kh) * kMaxRowGroups];
@@ -946,7 +1006,6 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         r_num[i] = 0.f;
         r_den[i] = 0.f;
     }
-    const int n_mine = (G * D - tid + 255) / 256;       // elements of this thread
     for (int sp = 0; sp < n_split; ++sp) {
         float vm[kPer], vl[kPer], vo[kPer];
         if (sp == split) {

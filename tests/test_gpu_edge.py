@@ -166,19 +166,24 @@ def test_errors_leave_state_unchanged():
 
 
 @pytest.mark.parametrize("portable", [False, True])
-def test_bitwise_deterministic(portable):
-    say("bitwise_deterministic", portable)
+@pytest.mark.parametrize("streams,window", [(4, 512), (64, 256)])
+def test_bitwise_deterministic(portable, streams, window):
+    """Repeated calls give identical bits: 4 streams take the multi-split merge
+    (epoch-tagged partials), 64 streams the two-split exchange."""
+    say("bitwise_deterministic", portable, streams, window)
     rng = np.random.default_rng(5)
-    tw = Twin(1, 4, 16, 2, 128, 512, 8, True, portable)
-    tw.reset(0, [0, 1000, 123456, 2**30], [0, 7, 300, 511])
-    for _ in range(700):
-        tw.gpu.append_kv(0, 0, 4, 1, to_device(rand(rng, 4, 1, 2, 128), True),
-                         to_device(rand(rng, 4, 1, 2, 128), True), want_bookkeeping=False)
-    q = to_device(rand(rng, 4, 16, 128), True)
-    o1, o2 = empty_out((4, 16, 128), True), empty_out((4, 16, 128), True)
-    tw.gpu.decode_attn(0, 0, 4, q, o1)
-    tw.gpu.decode_attn(0, 0, 4, q, o2)
-    assert bool((o1 == o2).all())
+    tw = Twin(1, streams, 16, 2, 128, window, 8, True, portable)
+    tw.reset(0, [(b * 7919 + b * b * 2**20) % 2**30 for b in range(streams)],
+             [(b * 97 + 7) % window for b in range(streams)])
+    k = to_device(rand(rng, streams, 8, 2, 128), True)
+    v = to_device(rand(rng, streams, 8, 2, 128), True)
+    for _ in range(window // 8 + 30):
+        tw.gpu.append_kv(0, 0, streams, 8, k, v, want_bookkeeping=False)
+    q = to_device(rand(rng, streams, 16, 128), True)
+    outs = [empty_out((streams, 16, 128), True) for _ in range(3)]
+    for o in outs:
+        tw.gpu.decode_attn(0, 0, streams, q, o)
+    assert bool((outs[0] == outs[1]).all()) and bool((outs[0] == outs[2]).all())
     tw.close()
 
 
