@@ -95,7 +95,7 @@ def summarize(args):
         rows_all = []
         for f in cc:
             rows_all += list(csv.DictReader(open(f)))
-        is_attn = lambda n: "decode_mfma" in n or "chunk_mfma" in n or "chunk_tiled" in n
+        is_attn = lambda n: "decode_mfma" in n or "chunk_mfma" in n or "chunk_tiled" in n or "chunk_pipe" in n
         last_attn = max([int(r["Dispatch_Id"]) for r in rows_all if is_attn(r["Kernel_Name"])] + [0])
         for r in rows_all:
             name = r["Kernel_Name"]

@@ -1902,6 +1902,458 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_tiled(Geometry g, int layer
     }
 }
 
+// ---------------------------------------------------------- pipelined chunk --
+// Visit rings of one wave group: K parts (the 32 raw K rows and the visit's
+// R(rho) row) and V parts in separate rings, and two rotated-K tiles.  At step
+// s a group rotates the keys of its visit s + 1 into one tile while it runs
+// QK^T, the online softmax and PV of visit s on the other, so a step has one
+// barrier and the rotation's VALU work overlaps the MFMAs.  K(v) is loaded
+// three steps before its rotation, V(v) two steps before its PV.
+template <int D>
+struct PipeBuf {
+    static constexpr int kK = kTile * D * 2;           // raw K rows, row r at r * 2D bytes
+    static constexpr int kC = D * 4;                   // the R(rho) row (D/2 float2)
+    static constexpr int kKC = kK + kC;                 // one K slot
+    static constexpr int kV = kTile * D * 2;           // V chunks, as in the decode buffers
+    static constexpr int kT = kTile * D * 2;           // a rotated-K tile (XOR-swizzled rows)
+    static constexpr int dK = 3, dV = 3;               // ring depths
+    static constexpr int kGroup = dK * kKC + dV * kV + 2 * kT;
+    static constexpr int nK = 2 * (D / 32) / 4 + 1;    // DMA instructions per wave: K rows + row quarter
+    static constexpr int nV = (D / 16) / 4;
+};
+
+template <int D, int NW, int WG>
+__global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer, StreamBatch st, int C,
+                                                     const uint16_t* __restrict__ q,
+                                                     uint16_t* __restrict__ out, int n_split) {
+    constexpr int KK = D / 32, NB = D / 16, HP = D / 64;
+    constexpr int P = D / 16;                          // rotation pairs per lane (8 lanes per key)
+    using PB = PipeBuf<D>;
+    __shared__ __align__(16) unsigned char lds_all[WG * PB::kGroup];
+    __shared__ __align__(16) unsigned char lds_rw[1024];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave_b = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wg = wave_b >> 2, wave = wave_b & 3;      // wave group, wave within the group
+    unsigned char* gb = lds_all + wg * PB::kGroup;
+    unsigned char* const ring_k = gb;                                   // dK slots
+    unsigned char* const ring_v = gb + PB::dK * PB::kKC;                // dV slots
+    unsigned char* const tiles = ring_v + PB::dV * PB::kV;              // 2 rotated tiles
+    const int n = lane & 15, gq = lane >> 4;
+    const int bi = blockIdx.z, kh = blockIdx.y, split = blockIdx.x;
+    const int b = st.b0 + bi, G = g.group, W = g.window;
+    const int rows = C * G;
+
+    DecodeCtx c;
+    const int L = st.length[bi];
+    c.L = L;
+    c.W = W;
+    c.oldest = st.next_slot[bi] - L < 0 ? st.next_slot[bi] - L + W : st.next_slot[bi] - L;
+    c.rq = L - C;                      // index of the chunk's first query
+    c.n_tiles = g.w_pad / kTile;
+    c.p0t = c.oldest / kTile;
+    c.t_o = c.oldest - c.p0t * kTile;
+    c.tb0 = 8 * (n >> 2) + (n & 3);
+    c.tb1 = c.tb0 + 4;
+    c.gq = gq;
+    c.n = n;
+    c.scale_log2 = g.scale_log2;
+    c.table = g.table;
+    const int64_t pair = pair_index(g, layer, b, kh);
+    c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
+    c.vp = (const uint16_t*)g.v_ring + pair * g.w_pad * D;
+    int n_visit;
+    {
+        int last = c.oldest + L - 1;
+        if (last < W) {
+            n_visit = last / kTile - c.p0t + 1;
+        } else {
+            last -= W;
+            n_visit = c.n_tiles - c.p0t + last / kTile + 1;
+            if (n_visit > c.n_tiles) n_visit = c.n_tiles;
+        }
+    }
+    const int per = (n_visit + n_split - 1) / n_split;
+    const int k0 = split * per, k1 = min(n_visit, k0 + per);
+    // group wg takes visits k0 + wg, k0 + wg + WG, ...: its local visit v is
+    // kvis(v); every wave of the block runs n_steps steps (one barrier each)
+    const int n_mine = k0 + wg < k1 ? (k1 - k0 - wg + WG - 1) / WG : 0;
+    const int n_steps = (k1 - k0 + WG - 1) / WG;
+    auto kvis = [&](int v) { return k0 + wg + WG * v; };
+
+    // this wave's quarter of local visit v's K part (rows + a quarter of the
+    // R(rho) row, |rho| for the first visit) and of its V part
+    auto issue_k = [&](int v, unsigned char* slot) {
+        const int kv = kvis(v);
+        const int p = visit_tile(c, kv);
+        const int s0 = p * kTile;
+        const unsigned char* krow = (const unsigned char*)(c.kp + (int64_t)s0 * D);
+#pragma unroll
+        for (int u = 0; u < PB::nK - 1; ++u) {
+            const int j = wave * (PB::nK - 1) + u;
+            dma16(krow + j * 1024 + 16 * lane, slot + j * 1024);
+        }
+        const int rho = visit_rho(c, kv, s0);
+        const unsigned char* row = (const unsigned char*)(c.table + (int64_t)(rho < 0 ? -rho : rho) * (D / 2));
+        constexpr int q4 = PB::kC / 4;                  // bytes of the row per wave
+        if (lane < q4 / 16) dma16(row + wave * q4 + 16 * lane, slot + PB::kK + wave * q4);
+    };
+    auto issue_v = [&](int v, unsigned char* slot) {
+        const int p = visit_tile(c, kvis(v));
+        const uint16_t* vb = c.vp + ((int64_t)(p * 4 + gq) * D + n) * 8;
+#pragma unroll
+        for (int u = 0; u < PB::nV; ++u) {
+            const int nb = wave * PB::nV + u;
+            dma16(vb + (int64_t)nb * 16 * 8, slot + nb * 1024);
+        }
+    };
+
+    // Prologue: R(W) into LDS (wave 0), register loads (query rows, their
+    // rotation rows, the lane's R(t) pairs), then K(0), K(1), V(0).
+    if (wave_b == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
+    const int kr_t = 8 * wave + (lane >> 3);           // key offset this lane rotates
+    const int kr_i = P * (lane & 7);                   // its first pair index
+    u32x4 qr[NW][KK];
+    float4 qc[NW][HP][4];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        int row = 16 * (wave + 4 * w) + n;
+        if (row >= rows) row = 0;
+        const int cc = row / G, h = kh * G + (row - cc * G);
+        const uint16_t* qp = q + (((int64_t)bi * C + cc) * g.hq + h) * D + 8 * gq;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qr[w][kk] = *(const u32x4*)(qp + 32 * kk);
+        load_coef<D>(g.table, c.rq + cc, gq, qc[w]);
+    }
+    float2 rt[P];
+    {
+        const float2* rp = g.table + (int64_t)kr_t * (D / 2) + kr_i;
+#pragma unroll
+        for (int i = 0; i < P; ++i) rt[i] = rp[i];
+    }
+    if (n_mine > 0) issue_k(0, ring_k);
+    if (n_mine > 1) issue_k(1, ring_k + PB::kKC);
+    if (n_mine > 0) issue_v(0, ring_v);
+
+    // queries rotated once, with the softmax scale folded into the rotation
+    // (one bf16 rounding, as without it), into MFMA B operands (zero rows pad)
+    bf16x8 qb[NW][KK];
+    int rq_col[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int row = 16 * (wave + 4 * w) + n;
+#pragma unroll
+        for (int kk = 0; kk < HP; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float4& f = qc[w][kk][j];
+                f = float4{f.x * c.scale_log2, f.y * c.scale_log2, f.z * c.scale_log2, f.w * c.scale_log2};
+            }
+        rotate_row<D>(qc[w], qr[w], qb[w]);
+        if (row >= rows) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qb[w][kk][e] = (__bf16)0.f;
+        }
+        rq_col[w] = row < rows ? c.rq + row / G : -1;
+    }
+    // column blocks with at least one real row (wave-uniform)
+    const bool act0 = 16 * wave < rows, act1 = NW > 1 && 16 * (wave + 4) < rows;
+
+    floatx4 o[NW][NB];
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) o[w][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m[NW], l[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        m[w] = kNegBig;
+        l[w] = 0.f;
+    }
+    const int r_last = L - 1;
+
+    // Rotates key kr_t of local visit v (pairs kr_i .. kr_i + P - 1) from its K
+    // slot into a rotated tile: R(rho + t) = R(rho) R(t); on the block's first
+    // visit of the ring (kv == 0) R(rho) = R(t_o) conjugated, and keys before
+    // the oldest slot (the window's newest) get R(W) on top.
+    auto rotate = [&](const unsigned char* kslot, unsigned char* tile, bool first, bool seam) {
+        const float4* br = (const float4*)(kslot + PB::kK) + kr_i / 2;
+        const unsigned char* kraw = kslot + kr_t * D * 2;
+        uint32_t x1w[P / 2], x2w[P / 2];
+        if constexpr (P == 8) {
+            const u32x4 a1 = *(const u32x4*)(kraw + 2 * kr_i), a2 = *(const u32x4*)(kraw + 2 * (kr_i + D / 2));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x1w[i] = a1[i];
+                x2w[i] = a2[i];
+            }
+        } else {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 a1 = *(const u32x2*)(kraw + 2 * kr_i), a2 = *(const u32x2*)(kraw + 2 * (kr_i + D / 2));
+            x1w[0] = a1[0];
+            x1w[1] = a1[1];
+            x2w[0] = a2[0];
+            x2w[1] = a2[1];
+        }
+        float2 cf[P];
+#pragma unroll
+        for (int i2 = 0; i2 < P / 2; ++i2) {
+            const float4 b4 = br[i2];
+            const float2 bs[2] = {float2{b4.x, b4.y}, float2{b4.z, b4.w}};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = 2 * i2 + h;
+                cf[i] = float2{bs[h].x * rt[i].x - bs[h].y * rt[i].y, bs[h].y * rt[i].x + bs[h].x * rt[i].y};
+            }
+        }
+        if (first) {                                   // wave-uniform, first visit of the ring only
+            const bool wrap = seam && kr_t < c.t_o;    // index kr_t - t_o + W: R(W) on top
+            const float4* wr = (const float4*)lds_rw + kr_i / 2;
+#pragma unroll
+            for (int i2 = 0; i2 < P / 2; ++i2) {
+                const float4 b4 = br[i2], w4 = wr[i2];
+                const float2 bs[2] = {float2{b4.x, -b4.y}, float2{b4.z, -b4.w}};
+                const float2 w2[2] = {float2{w4.x, w4.y}, float2{w4.z, w4.w}};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int i = 2 * i2 + h;
+                    const float2 a = {bs[h].x * rt[i].x - bs[h].y * rt[i].y, bs[h].y * rt[i].x + bs[h].x * rt[i].y};
+                    const float2 r = {w2[h].x * a.x - w2[h].y * a.y, w2[h].y * a.x + w2[h].x * a.y};
+                    cf[i] = wrap ? r : a;
+                }
+            }
+        }
+        __bf16 y1[P], y2[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const float x1 = (i & 1) ? hi_bf16(x1w[i >> 1]) : lo_bf16(x1w[i >> 1]);
+            const float x2 = (i & 1) ? hi_bf16(x2w[i >> 1]) : lo_bf16(x2w[i >> 1]);
+            y1[i] = (__bf16)(x1 * cf[i].x - x2 * cf[i].y);
+            y2[i] = (__bf16)(x2 * cf[i].x + x1 * cf[i].y);
+        }
+        // dims kr_i .. (16-byte column kr_i / 8) and + D/2 (column + D/16)
+        unsigned char* d1 = tile + 16 * k_pos<D>(kr_t, kr_i / 8) + 2 * (kr_i % 8);
+        unsigned char* d2 = tile + 16 * k_pos<D>(kr_t, (kr_i + D / 2) / 8) + 2 * (kr_i % 8);
+        if constexpr (P == 8) {
+            bf16x8 v1, v2;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                v1[i] = y1[i];
+                v2[i] = y2[i];
+            }
+            *(bf16x8*)d1 = v1;
+            *(bf16x8*)d2 = v2;
+        } else {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 v1, v2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v1[i] = y1[i];
+                v2[i] = y2[i];
+            }
+            *(bf16x4*)d1 = v1;
+            *(bf16x4*)d2 = v2;
+        }
+    };
+
+    // Step -1: the rotation of local visit 0 (nothing to compute yet); K(0)
+    // has landed once at most K(1) and V(0) are outstanding.
+    {
+        if (n_mine > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PB::nK + PB::nV));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();                  // every wave's quarter (and R(W))
+        __builtin_amdgcn_sched_barrier(0);
+        lds_fence();
+        if (n_mine > 2) issue_k(2, ring_k + 2 * PB::kKC);
+        if (n_mine > 1) issue_v(1, ring_v + PB::kV);
+        if (n_mine > 0) {
+            const int kv = kvis(0);
+            rotate(ring_k, tiles, kv == 0, kv == 0 && c.t_o > 0);
+        }
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+    }
+
+    // Step s: K(s + 1) and V(s) have landed once at most K(s + 2) and V(s + 1)
+    // (issued by step s - 1, if they exist) are outstanding; after the barrier
+    // every wave is done with step s - 1, so K slot s % 3 (rotated there) and
+    // V slot (s - 1) % 3 (used there) take K(s + 3) and V(s + 2).  Slot and
+    // tile indices repeat every 6 steps; S = s % 6 is a compile-time constant.
+    auto step = [&](auto sc, int s) {
+        constexpr int S = decltype(sc)::value;
+        const bool do_r = s + 1 < n_mine, do_c = s < n_mine;
+        if (do_c) {
+            const int after = (s + 2 < n_mine ? PB::nK : 0) + (do_r ? PB::nV : 0);
+            if (after == PB::nK + PB::nV) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PB::nK + PB::nV));
+            else if (after == PB::nV) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PB::nV));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        lds_fence();
+        if (s + 3 < n_mine) issue_k(s + 3, ring_k + (S % 3) * PB::kKC);
+        if (s + 2 < n_mine) issue_v(s + 2, ring_v + ((S + 2) % 3) * PB::kV);
+
+        const int kv = kvis(s);
+        const int p = visit_tile(c, kv);
+        const int s0 = p * kTile;
+        const int rho = visit_rho(c, kv, s0);
+        const bool seam = (kv == 0) && (c.t_o > 0);
+        const bool cmp = do_c && act0;                 // a wave without query rows only rotates
+        // QK^T of visit s first, so that the rotation's VALU work below runs
+        // while the MFMAs execute
+        floatx4 a0[NW], a1[NW];
+        u32x4 vv[NB];
+        if (cmp) {
+            const unsigned char* tile = tiles + (S % 2) * PB::kT;
+            bf16x8 kA[2][KK];
+            const u32x4* kt = (const u32x4*)tile;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                kA[0][kk] = __builtin_bit_cast(bf16x8, kt[k_pos<D>(c.tb0, gq + 4 * kk)]);
+                kA[1][kk] = __builtin_bit_cast(bf16x8, kt[k_pos<D>(c.tb1, gq + 4 * kk)]);
+            }
+            const u32x4* lb = (const u32x4*)(ring_v + (S % 3) * PB::kV) + lane;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) vv[nb] = lb[nb * 64];
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                a0[w] = floatx4{0.f, 0.f, 0.f, 0.f};
+                a1[w] = floatx4{0.f, 0.f, 0.f, 0.f};
+                if (w == 1 && !act1) continue;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    a0[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[0][kk], qb[w][kk], a0[w], 0, 0, 0);
+                    a1[w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[1][kk], qb[w][kk], a1[w], 0, 0, 0);
+                }
+            }
+        }
+        if (do_r) rotate(ring_k + ((S + 1) % 3) * PB::kKC, tiles + ((S + 1) % 2) * PB::kT, false, false);
+        if (cmp) {
+            const bool full = (kv != 0) && (rho + kTile <= c.rq + 1) && (s0 + kTile <= W);
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                if (w == 1 && !act1) break;
+                float s8[8] = {a0[w][0], a0[w][1], a0[w][2], a0[w][3], a1[w][0], a1[w][1], a1[w][2], a1[w][3]};
+                if (!full) {
+                    // branch-free: key index r of each score, then a select
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int tt = 8 * gq + e;
+                        const int r = rho + tt + ((seam & (tt < c.t_o)) ? W : 0);
+                        const bool ok = (r >= 0) & (r <= r_last) & ((rq_col[w] < 0) | (r <= rq_col[w])) &
+                                        (s0 + tt < W);
+                        s8[e] = ok ? s8[e] : -INFINITY;
+                    }
+                }
+                float mx = s8[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s8[e]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const bool grow = mx > m[w] + 8.f;       // lazy rescale, wave-uniform branch
+                if (__any(grow)) {
+                    const float mn = grow ? mx : m[w];
+                    const float alpha = fast_exp2(m[w] - mn);
+                    l[w] *= alpha;
+#pragma unroll
+                    for (int i = 0; i < NB; ++i) o[w][i] *= alpha;
+                    m[w] = mn;
+                }
+                bf16x8 pb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pe = fast_exp2(s8[e] - m[w]);
+                    l[w] += pe;
+                    pb[e] = (__bf16)pe;
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    o[w][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv[nb]), pb,
+                                                                       o[w][nb], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kLgkm0);            // the rotated tile is written
+    };
+    using std::integral_constant;
+    for (int s = 0; s < n_steps; s += 6) {
+        step(integral_constant<int, 0>{}, s);
+        if (s + 1 < n_steps) step(integral_constant<int, 1>{}, s + 1);
+        if (s + 2 < n_steps) step(integral_constant<int, 2>{}, s + 2);
+        if (s + 3 < n_steps) step(integral_constant<int, 3>{}, s + 3);
+        if (s + 4 < n_steps) step(integral_constant<int, 4>{}, s + 4);
+        if (s + 5 < n_steps) step(integral_constant<int, 5>{}, s + 5);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // this block's partial for the wave's rows: O^T element (dim 16 nb + 4 gq + j,
+    // column n) in o[w][nb][j]
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        l[w] += __shfl_xor(l[w], 16);
+        l[w] += __shfl_xor(l[w], 32);
+    }
+    if constexpr (WG == 2) {
+        // group 1 hands its (m, l, O) of every row to group 0 through LDS
+        float* xo = (float*)lds_all;                          // [row][D]
+        float* xml = xo + 4 * NW * 16 * D;                    // [row][2]
+        static_assert((4 * NW * 16 * D + 4 * NW * 16 * 2) * 4 <= WG * PB::kGroup, "merge buffer does not fit");
+        __syncthreads();
+        if (wg == 1) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int lr = 16 * (wave + 4 * w) + n;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    *(float4*)&xo[lr * D + 16 * nb + 4 * gq] = float4{o[w][nb][0], o[w][nb][1], o[w][nb][2], o[w][nb][3]};
+                if (gq == 0) *(float2*)&xml[lr * 2] = float2{m[w], l[w]};
+            }
+        }
+        __syncthreads();
+        if (wg == 1) return;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int lr = 16 * (wave + 4 * w) + n;
+            const float2 ml1 = *(const float2*)&xml[lr * 2];
+            const float mn = fmaxf(m[w], ml1.x);
+            const float a0 = exp2f(m[w] - mn), a1 = exp2f(ml1.x - mn);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float4 x = *(const float4*)&xo[lr * D + 16 * nb + 4 * gq];
+                o[w][nb][0] = o[w][nb][0] * a0 + x.x * a1;
+                o[w][nb][1] = o[w][nb][1] * a0 + x.y * a1;
+                o[w][nb][2] = o[w][nb][2] * a0 + x.z * a1;
+                o[w][nb][3] = o[w][nb][3] * a0 + x.w * a1;
+            }
+            l[w] = l[w] * a0 + ml1.y * a1;
+            m[w] = mn;
+        }
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int row = 16 * (wave + 4 * w) + n;
+        if (row >= rows) continue;
+        const int cc = row / G, h = kh * G + (row - cc * G);
+        if (n_split == 1) {
+            const float inv = 1.f / l[w];
+            uint16_t* op = out + (((int64_t)bi * C + cc) * g.hq + h) * D;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) op[16 * nb + 4 * gq + j] = f32_to_bf16_bits(o[w][nb][j] * inv);
+        } else {
+            // partials for combine_kernel (launched next on the same stream)
+            const int64_t pr = part_row(g, bi, kh, split, row);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                *(float4*)&g.part_o[pr * D + 16 * nb + 4 * gq] =
+                    float4{o[w][nb][0], o[w][nb][1], o[w][nb][2], o[w][nb][3]};
+            if (gq == 0) *(float2*)&g.part_ml[pr * 2] = float2{m[w], l[w]};
+        }
+    }
+}
+
 int env_int(const char* name, int dflt) {
     const char* s = getenv(name);
     return s ? atoi(s) : dflt;
@@ -1975,6 +2427,25 @@ hipError_t run_chunk_mfma_nq(const Geometry& g, int layer, const StreamBatch& st
 }
 
 template <int D, int NW>
+hipError_t run_chunk_pipe(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q, void* out,
+                          int n_cu, hipStream_t s) {
+    static const int target = env_int("A8R_DEBUG_CHUNK_BLOCKS", 0);
+    static const int groups = env_int("A8R_DEBUG_CHUNK_GROUPS", 2);
+    const int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, target > 0 ? target : n_cu, 4);
+    if (groups == 2)
+        hipLaunchKernelGGL((chunk_pipe<D, NW, 2>), dim3(n_split, g.hkv, st.nb), dim3(512), 0, s, g, layer, st,
+                           n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
+    else
+        hipLaunchKernelGGL((chunk_pipe<D, NW, 1>), dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st,
+                           n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_split == 1) return e;
+    // the splits' partials are merged by a second, chip-wide kernel
+    hipLaunchKernelGGL((combine_kernel<D, 2>), dim3(st.nb * n_q * g.hq), dim3(D), 0, s, g, n_q, n_split, out);
+    return hipGetLastError();
+}
+
+template <int D, int NW>
 hipError_t run_chunk_tiled(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q, void* out,
                            int n_cu, hipStream_t s) {
     static const int target = env_int("A8R_DEBUG_CHUNK_BLOCKS", 0);
@@ -2025,7 +2496,15 @@ hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now
         return g.d == 128 ? run_decode_mfma<128>(g, layer, now, q, out, n_cu, nullptr, nullptr, s)
                           : run_decode_mfma<64>(g, layer, now, q, out, n_cu, nullptr, nullptr, s);
     static const int tiled = env_int("A8R_DEBUG_CHUNK_TILED", 1);
-    if (allow_mfma && mfma_chunk_ok(g, n_q) && tiled) {
+    if (allow_mfma && mfma_chunk_ok(g, n_q) && tiled == 1) {
+        const bool one = n_q * g.group <= 64;
+        if (g.d == 128)
+            return one ? run_chunk_pipe<128, 1>(g, layer, now, n_q, q, out, n_cu, s)
+                       : run_chunk_pipe<128, 2>(g, layer, now, n_q, q, out, n_cu, s);
+        return one ? run_chunk_pipe<64, 1>(g, layer, now, n_q, q, out, n_cu, s)
+                   : run_chunk_pipe<64, 2>(g, layer, now, n_q, q, out, n_cu, s);
+    }
+    if (allow_mfma && mfma_chunk_ok(g, n_q) && tiled == 2) {
         const bool one = n_q * g.group <= 64;
         if (g.d == 128)
             return one ? run_chunk_tiled<128, 1>(g, layer, now, n_q, q, out, n_cu, s)
