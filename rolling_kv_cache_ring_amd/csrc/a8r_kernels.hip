@@ -151,18 +151,21 @@ __device__ __forceinline__ int64_t part_row(const Geometry& g, int bi, int kh, i
     return (((int64_t)bi * g.hkv + kh) * kMaxSplits + split) * g.rows_max + row;
 }
 
-// One block per output row (stream, query, head); D threads, one per dim.
+// Merges the splits' partials: 256 threads, each 4 consecutive dims of one
+// output row (stream, query, head); D/4 threads per row.  Every split's loads
+// are issued together (one round trip), then combined in split order.
 template <int D, int EB>
-__global__ __launch_bounds__(128) void combine_kernel(Geometry g, int n_q, int n_split, void* out) {
-    const int o = blockIdx.x;
+__global__ __launch_bounds__(256) void combine_kernel(Geometry g, int n_q, int n_split, void* out, int rows) {
+    constexpr int TPR = D / 4, RPB = 256 / TPR;          // threads per row, rows per block
+    const int o = blockIdx.x * RPB + threadIdx.x / TPR;
+    const int d4 = threadIdx.x % TPR;
+    if (o >= rows) return;
     const int h = o % g.hq;
     const int c = (o / g.hq) % n_q;
     const int bi = o / (g.hq * n_q);
     const int kh = h / g.group, row = c * g.group + (h - kh * g.group);
-    const int d = threadIdx.x;
-    // every split's loads are issued together (one round trip), then combined
-    // in split order
-    float mv[kMaxSplits], lv[kMaxSplits], ov[kMaxSplits];
+    float mv[kMaxSplits], lv[kMaxSplits];
+    float4 ov[kMaxSplits];
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
         if (s < n_split) {
@@ -170,23 +173,40 @@ __global__ __launch_bounds__(128) void combine_kernel(Geometry g, int n_q, int n
             const float2 ml = *(const float2*)&g.part_ml[pr * 2];
             mv[s] = ml.x;
             lv[s] = ml.y;
-            ov[s] = g.part_o[pr * D + d];
+            ov[s] = *(const float4*)&g.part_o[pr * D + 4 * d4];
         }
     }
     float mmax = kNegBig;
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s)
         if (s < n_split) mmax = fmaxf(mmax, mv[s]);
-    float num = 0.f, den = 0.f;
+    float den = 0.f;
+    float4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) {
         if (s < n_split) {
             const float w = exp2f(mv[s] - mmax);
             den += w * lv[s];
-            num += w * ov[s];
+            num.x += w * ov[s].x;
+            num.y += w * ov[s].y;
+            num.z += w * ov[s].z;
+            num.w += w * ov[s].w;
         }
     }
-    store_elem<EB>(out, (((int64_t)bi * n_q + c) * g.hq + h) * D + d, num / den);
+    const int64_t ob = (((int64_t)bi * n_q + c) * g.hq + h) * D + 4 * d4;
+    store_elem<EB>(out, ob, num.x / den);
+    store_elem<EB>(out, ob + 1, num.y / den);
+    store_elem<EB>(out, ob + 2, num.z / den);
+    store_elem<EB>(out, ob + 3, num.w / den);
+}
+
+template <int D, int EB>
+hipError_t launch_combine(const Geometry& g, int nb, int n_q, int n_split, void* out, hipStream_t s) {
+    constexpr int RPB = 256 / (D / 4);
+    const int rows = nb * n_q * g.hq;
+    hipLaunchKernelGGL((combine_kernel<D, EB>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, g, n_q, n_split,
+                       out, rows);
+    return hipGetLastError();
 }
 
 // --------------------------------------------------------- portable path ----
@@ -1931,6 +1951,8 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     using PB = PipeBuf<D>;
     __shared__ __align__(16) unsigned char lds_all[WG * PB::kGroup];
     __shared__ __align__(16) unsigned char lds_rw[1024];
+    __shared__ __align__(16) unsigned char lds_qc[8 * 1024];        // R(L - C + c) rows, c < C
+    static_assert(kMaxPartialQ * D * 4 <= 8 * 1024, "query rotation rows do not fit");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave_b = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1983,8 +2005,10 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
 
     // this wave's quarter of local visit v's K part (rows + a quarter of the
     // R(rho) row, |rho| for the first visit) and of its V part
+    // (a v past the group's visits loads the pair's first tile instead, which
+    // is always in range; its slot is never read)
     auto issue_k = [&](int v, unsigned char* slot) {
-        const int kv = kvis(v);
+        const int kv = v < n_mine ? kvis(v) : 0;
         const int p = visit_tile(c, kv);
         const int s0 = p * kTile;
         const unsigned char* krow = (const unsigned char*)(c.kp + (int64_t)s0 * D);
@@ -1999,7 +2023,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         if (lane < q4 / 16) dma16(row + wave * q4 + 16 * lane, slot + PB::kK + wave * q4);
     };
     auto issue_v = [&](int v, unsigned char* slot) {
-        const int p = visit_tile(c, kvis(v));
+        const int p = visit_tile(c, v < n_mine ? kvis(v) : 0);
         const uint16_t* vb = c.vp + ((int64_t)(p * 4 + gq) * D + n) * 8;
 #pragma unroll
         for (int u = 0; u < PB::nV; ++u) {
@@ -2008,13 +2032,14 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         }
     };
 
-    // Prologue: R(W) into LDS (wave 0), register loads (query rows, their
-    // rotation rows, the lane's R(t) pairs), then K(0), K(1), V(0).
-    if (wave_b == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
+    // Prologue: register loads (query rows, the lane's R(t) pairs), R(W) into
+    // LDS (wave 0), the C consecutive table rows of the queries' rotations into
+    // LDS (1 KiB per wave, clamped to them), then K(0), K(1), V(0), issued even
+    // where those visits do not exist (then they re-read an in-range tile), so
+    // that the first wait below is unconditional.
     const int kr_t = 8 * wave + (lane >> 3);           // key offset this lane rotates
     const int kr_i = P * (lane & 7);                   // its first pair index
     u32x4 qr[NW][KK];
-    float4 qc[NW][HP][4];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         int row = 16 * (wave + 4 * w) + n;
@@ -2023,7 +2048,6 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         const uint16_t* qp = q + (((int64_t)bi * C + cc) * g.hq + h) * D + 8 * gq;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qr[w][kk] = *(const u32x4*)(qp + 32 * kk);
-        load_coef<D>(g.table, c.rq + cc, gq, qc[w]);
     }
     float2 rt[P];
     {
@@ -2031,33 +2055,17 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
 #pragma unroll
         for (int i = 0; i < P; ++i) rt[i] = rp[i];
     }
-    if (n_mine > 0) issue_k(0, ring_k);
-    if (n_mine > 1) issue_k(1, ring_k + PB::kKC);
-    if (n_mine > 0) issue_v(0, ring_v);
-
-    // queries rotated once, with the softmax scale folded into the rotation
-    // (one bf16 rounding, as without it), into MFMA B operands (zero rows pad)
-    bf16x8 qb[NW][KK];
-    int rq_col[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int row = 16 * (wave + 4 * w) + n;
-#pragma unroll
-        for (int kk = 0; kk < HP; ++kk)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float4& f = qc[w][kk][j];
-                f = float4{f.x * c.scale_log2, f.y * c.scale_log2, f.z * c.scale_log2, f.w * c.scale_log2};
-            }
-        rotate_row<D>(qc[w], qr[w], qb[w]);
-        if (row >= rows) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qb[w][kk][e] = (__bf16)0.f;
-        }
-        rq_col[w] = row < rows ? c.rq + row / G : -1;
+    if (wave_b == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
+    {
+        const int qcb = C * D * 4;
+        int off = wave_b * 1024 + 16 * lane;
+        off = off < qcb ? off : qcb - 16;
+        dma16((const unsigned char*)(g.table + (int64_t)c.rq * (D / 2)) + off, lds_qc + wave_b * 1024);
     }
+    issue_k(0, ring_k);
+    issue_k(1, ring_k + PB::kKC);
+    issue_v(0, ring_v);
+
     // column blocks with at least one real row (wave-uniform)
     const bool act0 = 16 * wave < rows, act1 = NW > 1 && 16 * (wave + 4) < rows;
 
@@ -2161,8 +2169,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     // Step -1: the rotation of local visit 0 (nothing to compute yet); K(0)
     // has landed once at most K(1) and V(0) are outstanding.
     {
-        if (n_mine > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PB::nK + PB::nV));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PB::nK + PB::nV));
         __builtin_amdgcn_s_barrier();                  // every wave's quarter (and R(W))
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
@@ -2173,6 +2180,32 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
             rotate(ring_k, tiles, kv == 0, kv == 0 && c.t_o > 0);
         }
         __builtin_amdgcn_s_waitcnt(kLgkm0);
+    }
+
+    // queries rotated once, with the softmax scale folded into the rotation
+    // (one bf16 rounding, as without it), into MFMA B operands (zero rows pad)
+    bf16x8 qb[NW][KK];
+    int rq_col[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int row = 16 * (wave + 4 * w) + n;
+        float4 qc[HP][4];
+        lds_coef<D>(lds_qc + (row < rows ? row / G : 0) * D * 4, gq, qc);
+#pragma unroll
+        for (int kk = 0; kk < HP; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float4& f = qc[kk][j];
+                f = float4{f.x * c.scale_log2, f.y * c.scale_log2, f.z * c.scale_log2, f.w * c.scale_log2};
+            }
+        rotate_row<D>(qc, qr[w], qb[w]);
+        if (row >= rows) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qb[w][kk][e] = (__bf16)0.f;
+        }
+        rq_col[w] = row < rows ? c.rq + row / G : -1;
     }
 
     // Step s: K(s + 1) and V(s) have landed once at most K(s + 2) and V(s + 1)
@@ -2388,9 +2421,7 @@ hipError_t run_portable(const Geometry& g, int layer, const StreamBatch& st, int
                        layer, st, n_q, q, out, n_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split == 1) return e;
-    hipLaunchKernelGGL((combine_kernel<D, EB>), dim3(st.nb * n_q * g.hq), dim3(D), 0, s, g, n_q, n_split,
-                       out);
-    return hipGetLastError();
+    return launch_combine<D, EB>(g, st.nb, n_q, n_split, out, s);
 }
 
 template <int D>
@@ -2441,8 +2472,7 @@ hipError_t run_chunk_pipe(const Geometry& g, int layer, const StreamBatch& st, i
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split == 1) return e;
     // the splits' partials are merged by a second, chip-wide kernel
-    hipLaunchKernelGGL((combine_kernel<D, 2>), dim3(st.nb * n_q * g.hq), dim3(D), 0, s, g, n_q, n_split, out);
-    return hipGetLastError();
+    return launch_combine<D, 2>(g, st.nb, n_q, n_split, out, s);
 }
 
 template <int D, int NW>
@@ -2461,8 +2491,7 @@ hipError_t run_chunk_tiled(const Geometry& g, int layer, const StreamBatch& st, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split == 1) return e;
     // the splits' partials are merged by a second, chip-wide kernel
-    hipLaunchKernelGGL((combine_kernel<D, 2>), dim3(st.nb * n_q * g.hq), dim3(D), 0, s, g, n_q, n_split, out);
-    return hipGetLastError();
+    return launch_combine<D, 2>(g, st.nb, n_q, n_split, out, s);
 }
 
 bool mfma_chunk_ok(const Geometry& g, int n_q) {
