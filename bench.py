@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen3b_batch64", choices=["qwen3b_batch64", "qwen3b_chunk8"])
+    ap.add_argument("--workload", default="qwen3b_batch64", choices=["qwen3b_batch64", "qwen3b_chunk8", "qwen3b_chunk12", "qwen3b_chunk16"])
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
                     help="decode step per layer as one a8r_append_decode_attn call (fused) or as "
                          "a8r_append_kv + a8r_decode_attn (separate)")

@@ -111,14 +111,19 @@ WORKLOADS = {
                                notes="36 layers, 64 streams, 16/2 heads, D=128, bf16, W=4096"),
     "qwen3b_chunk8": Workload(4, "qwen3b_chunk8", 36, 16, 16, 2, 128, 8192, True, 2000, chunk=8,
                               notes="36 layers, 16 streams, W=8192, 8 positions per clock"),
+    # the same stream at 120 ms and 160 ms clocks (12 and 16 new positions per call)
+    "qwen3b_chunk12": Workload(5, "qwen3b_chunk12", 36, 16, 16, 2, 128, 8192, True, 1334, chunk=12,
+                               notes="36 layers, 16 streams, W=8192, 12 positions per clock"),
+    "qwen3b_chunk16": Workload(6, "qwen3b_chunk16", 36, 16, 16, 2, 128, 8192, True, 1000, chunk=16,
+                               notes="36 layers, 16 streams, W=8192, 16 positions per clock"),
 }
 
 
 def start_states(workload: Workload) -> tuple[np.ndarray, np.ndarray]:
     """Per-stream (absolute start position P0, ring offset R0), seeded.
 
-    The batched workload draws P0 ~ U[0, 1e6) and R0 ~ U[0, W); the chunked one
-    starts every stream just below 2**24 (P0 ~ U[2**24 - W, 2**24)) with R0 = P0
+    The batched workload draws P0 ~ U[0, 1e6) and R0 ~ U[0, W); the chunked ones
+    start every stream just below 2**24 (P0 ~ U[2**24 - W, 2**24)) with R0 = P0
     mod W; the others start at P0 = 0, R0 = 0.
     """
     ss = np.random.SeedSequence([SEED_ROOT, workload.workload_id, 0xFFFFFFFF])
@@ -127,7 +132,7 @@ def start_states(workload: Workload) -> tuple[np.ndarray, np.ndarray]:
     if workload.name == "qwen3b_batch64":
         p0 = rng.integers(0, 1_000_000, size=n, dtype=np.int64)
         r0 = rng.integers(0, workload.window, size=n, dtype=np.int64)
-    elif workload.name == "qwen3b_chunk8":
+    elif workload.name.startswith("qwen3b_chunk"):
         p0 = rng.integers(2**24 - workload.window, 2**24, size=n, dtype=np.int64)
         r0 = p0 % workload.window
     else:

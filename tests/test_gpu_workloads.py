@@ -11,7 +11,8 @@
                   9.66 GB of ring): batched append + decode calls over all 64
                   streams, outputs of 9 sampled (layer, stream) pairs checked;
 * qwen3b_chunk8   full size (16 streams, W = 8192, positions crossing 2**24),
-                  batched 8-token append + chunk attention, sampled pairs checked.
+                  batched 8-token append + chunk attention, sampled pairs checked;
+* qwen3b_chunk12/16  the same at 12 and 16 positions per call.
 Inputs are the seeded N(0, 1) draws of ``synth``; unsampled pairs of the full
 size workloads are filled with other device-side random values that are never
 compared (only their finiteness is).
@@ -197,3 +198,11 @@ def test_qwen3b_batch64_full_size(fused):
 def test_qwen3b_chunk8_full_size():
     wl = W_["qwen3b_chunk8"]
     _full_size(wl, [0, 35], [0, 9, 15], 2, 8)
+
+
+@pytest.mark.parametrize("name", ["qwen3b_chunk12", "qwen3b_chunk16"])
+def test_qwen3b_clock_variants_full_size(name):
+    """The 120 ms and 160 ms clocks: 12 and 16 new positions per call (96 and
+    128 query rows per KV head)."""
+    wl = W_[name]
+    _full_size(wl, [0, 35], [0, 7, 15], 2, wl.chunk)
