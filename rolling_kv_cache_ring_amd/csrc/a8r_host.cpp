@@ -174,7 +174,7 @@ a8r_status compute_layout(const a8r_config* c, Layout* lay) {
     lay->part_ml_off = off;
     off = a8r::align_up(off + prow * 2 * 4, a8r::kAlign);
     lay->counter_off = off;
-    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kMaxRowGroups * sizeof(int),
+    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * sizeof(int),
                         a8r::kAlign);
     lay->part_t_off = off;
     off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kMaxSplits * a8r::kMaxGroupTagged *

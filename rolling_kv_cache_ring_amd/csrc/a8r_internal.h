@@ -32,7 +32,6 @@ constexpr int kMaxSplits = 16;     // most key splits per (stream, KV head)
 constexpr int kMaxPartialQ = 16;   // chunk sizes above this run without splits
 constexpr size_t kAlign = 256;
 constexpr int kBatch = 128;        // streams per launch (their state travels in the arguments)
-constexpr int kMaxRowGroups = 4;   // query row groups of one KV head in the chunk kernel
 constexpr int kMaxGroupTagged = 16;   // query heads per KV head in the MFMA decode kernel
 constexpr uint64_t kSlotEmpty = ~(uint64_t)0;   // an exchange slot holding no partial
 
@@ -60,7 +59,7 @@ struct Geometry {
     DevState* state;
     float* part_o;      // split partials: [n_streams][n_kv_heads][kMaxSplits][rows_max][D]
     float* part_ml;     // [n_streams][n_kv_heads][kMaxSplits][rows_max][2]
-    int* counters;      // [n_streams][n_kv_heads][kMaxRowGroups] split arrival counters, 0 between calls
+    int* counters;      // [n_streams][n_kv_heads] decode split arrival counters, 0 between calls
     uint64_t* part_t;   // decode split partials tagged with the launch epoch (high word):
                         // [n_streams][n_kv_heads][kMaxSplits][kMaxGroupTagged][D + 2] (O..., m, l)
     uint64_t* part_x;   // two-split decode exchange slots, one per output element:

@@ -14,10 +14,16 @@
 //   append_kernel      copies new K/V rows into their ring slots (one block per
 //                      stream) and records the new state
 //   attn_portable      any dtype / group size / chunk size; LDS-tiled VALU
-//   combine_kernel     merges split-K partials {m, l, O} of attn_portable
+//   combine_kernel     merges split-K partials {m, l, O} of attn_portable,
+//                      and chunk_pipe
 //   decode_mfma        bf16 decode (optionally fused with the append of the
 //                      new token); QK^T and PV on v_mfma_f32_16x16x32_bf16,
-//                      split-K partials merged by the last block to finish
+//                      split-K partials merged inside the kernel (two splits:
+//                      per-element atomic exchange; more: the last block)
+//   chunk_pipe         bf16 chunks of 2..16 positions (query rows of a KV head
+//                      in groups of up to 128 per block): keys rotated once
+//                      per visit into an LDS tile, QK^T and PV on MFMA,
+//                      software-pipelined
 //
 // Every kernel takes the ring state of its streams from its launch arguments
 // (StreamBatch, filled by the host from its bookkeeping when the call is made).
@@ -1006,7 +1012,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     }
 
     __syncthreads();            // every store of the block has been issued
-    int* counter = &g.counters[(bi * g.hkv + kh) * kMaxRowGroups];
+    int* counter = &g.counters[bi * g.hkv + kh];
     if (tid == 0) {
         const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == n_split - 1);
@@ -1085,409 +1091,14 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ------------------------------------------------------------- MFMA chunk ----
-// bf16 attention for C new positions per stream (several per audio clock) in
-// one block per (stream, KV head, split) and group of up to 64 query rows: the
-// C x G query rows of a KV head (row = c*G + hg) form NQ column blocks of 16, so
-// QK^T and PV are real contractions on v_mfma_f32_16x16x32_bf16 (8 positions x
-// 8 heads = 64 rows, NQ = 4, in one block: every K/V tile is read once).
-//
-// Same ring walk, memory pipeline (LDS DMA, K and V parts, exact waits) and
-// split merge as decode_mfma.  The rotation is split differently: each query
-// row is rotated once, by its own re-based index r_q(c) = L - C + c, in the
-// prologue; each key row is rotated by R(rho + t), composed per visit from
-// R(rho) (the table row staged with the visit's K part) and the lane's R(t)
-// (registers):  (c, s)(a + b) = (c_a c_b - s_a s_b, s_a c_b + c_a s_b).  On the
-// first visit rho = -t_o: R(-t_o) is R(t_o) conjugated, and the window's newest
-// keys that share the oldest key's tile (offsets t < t_o, index t - t_o + W)
-// get R(W) composed on top.  Query c sees keys with index <= r_q(c): causal
-// inside the chunk, the whole older window before it.
-template <int D>
-__device__ __forceinline__ void compose(const float4 (&a)[D / 64][4], const float4 (&b)[D / 64][4],
-                                        float4 (&out)[D / 64][4]) {
-#pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 x = a[kk][j], y = b[kk][j];
-            out[kk][j] = float4{x.x * y.x - x.y * y.y, x.y * y.x + x.x * y.y,
-                                x.z * y.z - x.w * y.w, x.w * y.z + x.z * y.w};
-        }
-}
-
-template <int D, int NQ>
-__global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, StreamBatch st, int C,
-                                                     const uint16_t* __restrict__ q,
-                                                     uint16_t* __restrict__ out, int n_split) {
-    // NQ column blocks of 16 query rows per block; row group rg covers rows
-    // 16*NQ*rg .. 16*NQ*(rg+1)-1 (blockIdx.x = rg * n_split + split)
-    constexpr int KK = D / 32, NB = D / 16, HP = D / 64;
-    using B = DecBuf<D>;
-    constexpr int kRows = 16 * NQ;
-    constexpr int kHalf = 4 * (B::kK + B::kV);   // buffers a (K, V) of the 4 waves; then b
-    // LDS: the visit buffers of the 4 waves (buffer b also stages the prologue
-    // inputs; after the walk the array holds the cross-wave merge), the
-    // rotated query rows in MFMA B-operand order (after the walk: the per-row
-    // (m, l) values), the R(W) row.
-    __shared__ __align__(16) unsigned char lds_kv[2 * kHalf];
-    __shared__ __align__(16) unsigned char q_lds[NQ * KK * 1024];
-    __shared__ __align__(16) unsigned char lds_rw[1024];
-    __shared__ int s_last;
-    static_assert(4 * kRows * D * 4 <= 2 * kHalf, "merge buffer does not fit");
-    static_assert(4 * kRows * 2 * 4 <= NQ * KK * 1024, "(m, l) buffer does not fit");
-    // staging in buffer b: raw query rows, R(r_q(c)) rows (1 KiB slots), R(t) rows
-    constexpr int kStQ = 0, kStRc = kRows * D * 2, kStRt = kStRc + kMaxPartialQ * 1024;
-    static_assert(kStRt + kTile * D * 4 <= kHalf, "staging does not fit");
-    float (*red_o)[kRows][D] = (float (*)[kRows][D])lds_kv;
-    float (*red_ml)[kRows][2] = (float (*)[kRows][2])q_lds;
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n = lane & 15, gq = lane >> 4;
-    const int bi = blockIdx.z, kh = blockIdx.y;
-    const int rg = blockIdx.x / n_split, split = blockIdx.x - rg * n_split;
-    const int b = st.b0 + bi, G = g.group, W = g.window;
-    const int rows = C * G;                       // query rows of this KV head
-    const int row0 = rg * kRows;                  // first row of this block
-    const int n_rows = min(kRows, rows - row0);   // rows this block handles
-    unsigned char* ka = lds_kv + wave * B::kK;
-    unsigned char* va = lds_kv + 4 * B::kK + wave * B::kV;
-    unsigned char* kb = lds_kv + kHalf + wave * B::kK;
-    unsigned char* vb = lds_kv + kHalf + 4 * B::kK + wave * B::kV;
-    unsigned char* stage = lds_kv + kHalf;
-
-    DecodeCtx c;
-    const int L = st.length[bi];
-    c.L = L;
-    c.W = W;
-    c.oldest = st.next_slot[bi] - L < 0 ? st.next_slot[bi] - L + W : st.next_slot[bi] - L;
-    c.rq = L - C;                      // index of the chunk's first query
-    c.n_tiles = g.w_pad / kTile;
-    c.p0t = c.oldest / kTile;
-    c.t_o = c.oldest - c.p0t * kTile;
-    c.tb0 = 8 * (n >> 2) + (n & 3);
-    c.tb1 = c.tb0 + 4;
-    c.gq = gq;
-    c.n = n;
-    c.scale_log2 = g.scale_log2;
-    c.table = g.table;
-    const int64_t pair = pair_index(g, layer, b, kh);
-    c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
-    c.vp = (const uint16_t*)g.v_ring + pair * g.w_pad * D;
-    int n_visit;
-    {
-        int last = c.oldest + L - 1;
-        if (last < W) {
-            n_visit = last / kTile - c.p0t + 1;
-        } else {
-            last -= W;
-            n_visit = c.n_tiles - c.p0t + last / kTile + 1;
-            if (n_visit > c.n_tiles) n_visit = c.n_tiles;
-        }
-    }
-    const int per = (n_visit + n_split - 1) / n_split;
-    const int k0 = split * per, k1 = min(n_visit, k0 + per);
-    int k = k0 + wave;
-
-    // Prologue (all LDS DMA): the block's raw query rows (rows past the chunk
-    // re-read row 0), the rows R(r_q(c)), R(t) for t < 32 and R(W), spread over
-    // the waves; then K(k), V(k); wait; every wave's.
-    {
-        constexpr int nq = kRows * D * 2 / 1024;
-        for (int j = wave; j < nq; j += 4) {
-            const int byte = j * 1024 + 16 * lane;
-            const int lr = byte / (D * 2), off = byte - lr * (D * 2);
-            int row = row0 + lr;
-            if (row >= rows) row = 0;
-            const int cc = row / G, h = kh * G + (row - cc * G);
-            dma16((const unsigned char*)(q + (((int64_t)bi * C + cc) * g.hq + h) * D) + off, stage + kStQ + j * 1024);
-        }
-        for (int cc = wave; cc < C; cc += 4) dma_table_row<D>(g.table, c.rq + cc, lane, stage + kStRc + cc * 1024);
-        constexpr int nrt = kTile * D * 4 / 1024;
-        for (int j = wave; j < nrt; j += 4)
-            dma16((const unsigned char*)g.table + j * 1024 + 16 * lane, stage + kStRt + j * 1024);
-        if (wave == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
-    }
-    if (k < k1) {
-        dec_load_k<D, true>(c, k, lane, ka);
-        dec_load_v<D>(c, k, va);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
-    } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    __builtin_amdgcn_s_barrier();
-    lds_fence();
-
-    // each wave rotates query column blocks cq = wave, wave + 4, ... by
-    // R(L - C + c) into q_lds (B-operand order); every lane keeps R(t) of its
-    // two key offsets
-    for (int cq = wave; cq < NQ; cq += 4) {
-        const int lr = 16 * cq + n, row = row0 + lr;
-        bf16x8 qb[KK];
-        if (row < rows) {
-            u32x4 qr[KK];
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) qr[kk] = *(const u32x4*)(stage + kStQ + lr * D * 2 + 16 * gq + 64 * kk);
-            float4 cq4[HP][4];
-            lds_coef<D>(stage + kStRc + (row / G) * 1024, gq, cq4);
-            rotate_row<D>(cq4, qr, qb);
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qb[kk][e] = (__bf16)0.f;
-        }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) *((bf16x8*)(q_lds + (cq * KK + kk) * 1024) + lane) = qb[kk];
-    }
-    float4 cf0[HP][4], cf1[HP][4];
-    lds_coef<D>(stage + kStRt + c.tb0 * D * 4, gq, cf0);
-    lds_coef<D>(stage + kStRt + c.tb1 * D * 4, gq, cf1);
-    // each column's query index for the causal mask (-1: padding row)
-    int rq_col[NQ];
-#pragma unroll
-    for (int cq = 0; cq < NQ; ++cq) {
-        const int row = row0 + 16 * cq + n;
-        rq_col[cq] = row < rows ? c.rq + row / G : -1;
-    }
-    __syncthreads();   // q_lds ready, staging consumed
-    if (k + 4 < k1) {
-        dec_load_k<D, true>(c, k + 4, lane, kb);
-        dec_load_v<D>(c, k + 4, vb);
-    }
-
-    floatx4 o[NQ][NB];
-#pragma unroll
-    for (int cq = 0; cq < NQ; ++cq)
-#pragma unroll
-        for (int i = 0; i < NB; ++i) o[cq][i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m[NQ], l[NQ];
-#pragma unroll
-    for (int cq = 0; cq < NQ; ++cq) {
-        m[cq] = kNegBig;
-        l[cq] = 0.f;
-    }
-    const int r_last = L - 1;   // the newest query's index
-
-    // scores of visit k for every column block, online softmax; probabilities
-    // (keys 8*gq .. 8*gq+7 of each column) in pb
-    auto scores = [&](int kv, const DecK<D>& rk, bf16x8 (&pb)[NQ]) {
-        const int p = visit_tile(c, kv);
-        const int s0 = p * kTile;
-        const int rho = visit_rho(c, kv, s0);
-        const bool seam = (kv == 0) && (c.t_o > 0);
-        float4 base[HP][4], ca[HP][4], cb[HP][4];
-#pragma unroll
-        for (int kk = 0; kk < HP; ++kk)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float4 x = rk.qc[kk][j];
-                base[kk][j] = kv == 0 ? float4{x.x, -x.y, x.z, -x.w} : x;   // R(-t_o) or R(rho)
-            }
-        compose<D>(base, cf0, ca);
-        compose<D>(base, cf1, cb);
-        if (seam) {
-            float4 rw[HP][4], t[HP][4];
-            lds_coef<D>(lds_rw, gq, rw);
-            if (c.tb0 < c.t_o) {
-                compose<D>(rw, ca, t);
-#pragma unroll
-                for (int kk = 0; kk < HP; ++kk)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) ca[kk][j] = t[kk][j];
-            }
-            if (c.tb1 < c.t_o) {
-                compose<D>(rw, cb, t);
-#pragma unroll
-                for (int kk = 0; kk < HP; ++kk)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) cb[kk][j] = t[kk][j];
-            }
-        }
-        bf16x8 k0b[KK], k1b[KK];
-        rotate_row<D>(ca, rk.k0, k0b);
-        rotate_row<D>(cb, rk.k1, k1b);
-        const bool full = (kv != 0) && (rho + kTile <= c.rq + 1) && (s0 + kTile <= W);
-        const bf16x8* qlb = (const bf16x8*)q_lds + lane;
-#pragma unroll
-        for (int cq = 0; cq < NQ; ++cq) {
-            floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const bf16x8 qv = qlb[(cq * KK + kk) * 64];
-                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0b[kk], qv, a0, 0, 0, 0);
-                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1b[kk], qv, a1, 0, 0, 0);
-            }
-            float s[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] *= c.scale_log2;
-            if (!full) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int tt = 8 * gq + e;
-                    int r = rho + tt;
-                    if (seam && tt < c.t_o) r += W;
-                    const bool ok = (r >= 0) && (r <= r_last) && (rq_col[cq] < 0 || r <= rq_col[cq]) &&
-                                    (s0 + tt < W);
-                    if (!ok) s[e] = -INFINITY;
-                }
-            }
-            float mx = s[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            if (mx > m[cq] + 8.f) {
-                const float alpha = exp2f(m[cq] - mx);
-                l[cq] *= alpha;
-#pragma unroll
-                for (int i = 0; i < NB; ++i) o[cq][i] *= alpha;
-                m[cq] = mx;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pe = exp2f(s[e] - m[cq]);
-                l[cq] += pe;
-                pb[cq][e] = (__bf16)pe;
-            }
-        }
-    };
-    auto pv = [&](const u32x4 (&v)[NB], const bf16x8 (&pb)[NQ]) {
-#pragma unroll
-        for (int cq = 0; cq < NQ; ++cq)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                o[cq][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[nb]), pb[cq],
-                                                                    o[cq][nb], 0, 0, 0);
-    };
-    auto wait_k = [&](int kk) {
-        if (kk + 4 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV + B::nK + B::nV));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
-        __builtin_amdgcn_sched_barrier(0);
-        lds_fence();
-    };
-    auto wait_v = [&](int kk) {
-        if (kk + 8 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nK + B::nV + B::nK));
-        else if (kk + 4 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nK + B::nV));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_sched_barrier(0);
-        lds_fence();
-    };
-    while (k < k1) {
-        DecK<D> rk;
-        u32x4 rv[NB];
-        bf16x8 pb[NQ];
-        wait_k(k);
-        dec_read_k<D>(c, ka, rk);
-        __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_k<D, true>(c, k + 8, lane, ka);
-        scores(k, rk, pb);
-        wait_v(k);
-        dec_read_v<D>(va, lane, rv);
-        __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_v<D>(c, k + 8, va);
-        pv(rv, pb);
-        k += 4;
-        if (k >= k1) break;
-        wait_k(k);
-        dec_read_k<D>(c, kb, rk);
-        __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_k<D, true>(c, k + 8, lane, kb);
-        scores(k, rk, pb);
-        wait_v(k);
-        dec_read_v<D>(vb, lane, rv);
-        __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_v<D>(c, k + 8, vb);
-        pv(rv, pb);
-        k += 4;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_fence();
-
-#pragma unroll
-    for (int cq = 0; cq < NQ; ++cq) {
-        l[cq] += __shfl_xor(l[cq], 16);
-        l[cq] += __shfl_xor(l[cq], 32);
-    }
-    __syncthreads();   // every wave is done with its visit buffers and the query rows
-#pragma unroll
-    for (int cq = 0; cq < NQ; ++cq) {
-        const int lr = 16 * cq + n;
-        if (gq == 0) {
-            red_ml[wave][lr][0] = m[cq];
-            red_ml[wave][lr][1] = l[cq];
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) red_o[wave][lr][16 * nb + 4 * gq + j] = o[cq][nb][j];
-    }
-    __syncthreads();
-    for (int idx = tid; idx < n_rows * D; idx += 256) {
-        const int lr = idx / D, d = idx - lr * D, row = row0 + lr;
-        float mm = red_ml[0][lr][0];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) mm = fmaxf(mm, red_ml[w][lr][0]);
-        float num = 0.f, den = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float f = exp2f(red_ml[w][lr][0] - mm);
-            num += f * red_o[w][lr][d];
-            den += f * red_ml[w][lr][1];
-        }
-        const int cc = row / G, h = kh * G + (row - cc * G);
-        if (n_split == 1) {
-            out[(((int64_t)bi * C + cc) * g.hq + h) * D + d] = f32_to_bf16_bits(num / den);
-        } else {
-            const int64_t pr = part_row(g, bi, kh, split, row);
-            __hip_atomic_store(&g.part_o[pr * D + d], num, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (d == 0) {
-                __hip_atomic_store(&g.part_ml[pr * 2], mm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&g.part_ml[pr * 2 + 1], den, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-    }
-    if (n_split == 1) return;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int* counter = &g.counters[(bi * g.hkv + kh) * kMaxRowGroups + rg];
-    if (tid == 0) {
-        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == n_split - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    for (int idx = tid; idx < n_rows * D; idx += 256) {
-        const int row = row0 + idx / D, d = idx % D;
-        float mm = kNegBig;
-        for (int sp = 0; sp < n_split; ++sp)
-            mm = fmaxf(mm, __hip_atomic_load(&g.part_ml[part_row(g, bi, kh, sp, row) * 2], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT));
-        float num = 0.f, den = 0.f;
-        for (int sp = 0; sp < n_split; ++sp) {
-            const int64_t pr = part_row(g, bi, kh, sp, row);
-            const float f =
-                exp2f(__hip_atomic_load(&g.part_ml[pr * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - mm);
-            den += f * __hip_atomic_load(&g.part_ml[pr * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            num += f * __hip_atomic_load(&g.part_o[pr * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        const int cc = row / G, h = kh * G + (row - cc * G);
-        out[(((int64_t)bi * C + cc) * g.hq + h) * D + d] = f32_to_bf16_bits(num / den);
-    }
-    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// ------------------------------------------------------- MFMA chunk, tiled ----
+// ---------------------------------------------------------- pipelined chunk --
 // bf16 attention for C new positions per stream, one block per (stream, KV
-// head, split) for all C x G query rows (<= 128; row = c*G + hg): wave w owns
-// the query column blocks w, w + 4 (16 rows each) for the whole walk, so its
-// accumulators stay small and no cross-wave merge is needed.  The 4 waves walk
-// the split's visits together over a ring of NBUF block-shared visit buffers
-// (LDS DMA, each wave issuing a quarter of every visit's loads); per visit:
-//   wait for the visit's loads, barrier; refill the buffer freed by the
-//   previous visit; each wave rotates 8 of the 32 keys into a shared rotated-K
-//   tile (XOR-swizzled for the MFMA operand reads); barrier; each wave runs
-//   QK^T, the online softmax and PV for its rows.
+// head, split, row group of up to 128 of the C x G query rows; row = c*G + hg;
+// more than one row group re-reads the window), in WG groups
+// of 4 waves that take alternate visits of the split and merge at the end.
+// Within a group wave w owns the query column blocks w, w + 4 (16 rows each)
+// for the whole walk, and each wave issues a quarter of every visit's loads
+// (LDS DMA).
 // Rotation: each query row is rotated once, by its own re-based index
 // r_q(c) = L - C + c; key t of a visit by R(rho + t) = R(rho) R(t), R(rho) from
 // the table row staged with the visit, R(t) held by the lane (each lane always
@@ -1498,431 +1109,7 @@ __global__ __launch_bounds__(256, 1) void chunk_mfma(Geometry g, int layer, Stre
 // before it.  With several splits each block writes its rows' partials
 // {m, l, O} and combine_kernel, launched next, merges them (a chip-wide merge
 // instead of one block reading every split's partials).
-template <int D>
-struct ChunkBuf {
-    static constexpr int kK = kTile * D * 2;           // raw K rows, row r at r * 2D bytes
-    static constexpr int kC = 4 * 1024;                // the R(rho) row, one copy per wave
-    static constexpr int kV = kTile * D * 2;           // V chunks, as in the decode buffers
-    static constexpr int kBytes = kK + kC + kV;
-    static constexpr int nK = 2 * (D / 32) / 4;        // DMA instructions per wave and visit
-    static constexpr int nV = (D / 16) / 4;
-    static constexpr int nI = nK + 1 + nV;
-    // visit buffers per wave group (loads of NBUF - 1 of the group's visits in flight)
-    template <int WG>
-    static constexpr int nbuf() { return WG == 1 ? (D == 128 ? 6 : 8) : (D == 128 ? 3 : 4); }
-};
-
-// s_waitcnt vmcnt(n * per) for n in [0, 7] (per is a compile-time count)
-template <int per>
-__device__ __forceinline__ void wait_visits(int n) {
-    switch (n) {
-        case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
-        case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(per)); break;
-        case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * per)); break;
-        case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * per)); break;
-        case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * per)); break;
-        case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * per)); break;
-        case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * per)); break;
-        default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * per)); break;
-    }
-}
-
-template <int D, int NW, int WG>
-__global__ __launch_bounds__(256 * WG, 1) void chunk_tiled(Geometry g, int layer, StreamBatch st, int C,
-                                                      const uint16_t* __restrict__ q,
-                                                      uint16_t* __restrict__ out, int n_split) {
-    constexpr int KK = D / 32, NB = D / 16, HP = D / 64;
-    constexpr int P = D / 16;                          // rotation pairs per lane (8 lanes per key)
-    using CB = ChunkBuf<D>;
-    constexpr int NBUF = CB::template nbuf<WG>();
-    __shared__ __align__(16) unsigned char lds_bufs[WG * NBUF * CB::kBytes];
-    __shared__ __align__(16) unsigned char lds_kts[WG * kTile * D * 2];   // rotated K of each group's visit
-    __shared__ __align__(16) unsigned char lds_rw[1024];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave_b = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wg = wave_b >> 2, wave = wave_b & 3;      // wave group, wave within the group
-    unsigned char* lds_buf = lds_bufs + wg * NBUF * CB::kBytes;
-    unsigned char* lds_kt = lds_kts + wg * kTile * D * 2;
-    const int n = lane & 15, gq = lane >> 4;
-    const int bi = blockIdx.z, kh = blockIdx.y, split = blockIdx.x;
-    const int b = st.b0 + bi, G = g.group, W = g.window;
-    const int rows = C * G;
-
-    DecodeCtx c;
-    const int L = st.length[bi];
-    c.L = L;
-    c.W = W;
-    c.oldest = st.next_slot[bi] - L < 0 ? st.next_slot[bi] - L + W : st.next_slot[bi] - L;
-    c.rq = L - C;                      // index of the chunk's first query
-    c.n_tiles = g.w_pad / kTile;
-    c.p0t = c.oldest / kTile;
-    c.t_o = c.oldest - c.p0t * kTile;
-    c.tb0 = 8 * (n >> 2) + (n & 3);
-    c.tb1 = c.tb0 + 4;
-    c.gq = gq;
-    c.n = n;
-    c.scale_log2 = g.scale_log2;
-    c.table = g.table;
-    const int64_t pair = pair_index(g, layer, b, kh);
-    c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
-    c.vp = (const uint16_t*)g.v_ring + pair * g.w_pad * D;
-    int n_visit;
-    {
-        int last = c.oldest + L - 1;
-        if (last < W) {
-            n_visit = last / kTile - c.p0t + 1;
-        } else {
-            last -= W;
-            n_visit = c.n_tiles - c.p0t + last / kTile + 1;
-            if (n_visit > c.n_tiles) n_visit = c.n_tiles;
-        }
-    }
-    const int per = (n_visit + n_split - 1) / n_split;
-    const int k0 = split * per, k1 = min(n_visit, k0 + per);
-
-    // this wave's quarter of a visit's loads into buffer `bf`
-    auto issue = [&](int kv, int bf) {
-        unsigned char* buf = lds_buf + bf * CB::kBytes;
-        const int p = visit_tile(c, kv);
-        const int s0 = p * kTile;
-        const unsigned char* krow = (const unsigned char*)(c.kp + (int64_t)s0 * D);
-#pragma unroll
-        for (int u = 0; u < CB::nK; ++u) {
-            const int j = wave * CB::nK + u;
-            dma16(krow + j * 1024 + 16 * lane, buf + j * 1024);
-        }
-        const int rho = visit_rho(c, kv, s0);
-        dma_table_row<D>(c.table, rho < 0 ? -rho : rho, lane, buf + CB::kK + wave * 1024);
-        const uint16_t* vb = c.vp + ((int64_t)(p * 4 + gq) * D + n) * 8;
-#pragma unroll
-        for (int u = 0; u < CB::nV; ++u) {
-            const int nb = wave * CB::nV + u;
-            dma16(vb + (int64_t)nb * 16 * 8, buf + CB::kK + CB::kC + nb * 1024);
-        }
-    };
-
-    // Prologue: R(W) into LDS (wave 0), register loads (query rows, their
-    // rotation rows, the lane's R(t) pairs), then the loads of the first
-    // NBUF - 1 visits; everything before a visit's loads has landed by the
-    // time the wait for that visit returns.
-    if (wave_b == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
-    const int kr_t = 8 * wave + (lane >> 3);           // key offset this lane rotates
-    const int kr_i = P * (lane & 7);                   // its first pair index
-    u32x4 qr[NW][KK];
-    float4 qc[NW][HP][4];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        int row = 16 * (wave + 4 * w) + n;
-        if (row >= rows) row = 0;
-        const int cc = row / G, h = kh * G + (row - cc * G);
-        const uint16_t* qp = q + (((int64_t)bi * C + cc) * g.hq + h) * D + 8 * gq;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qr[w][kk] = *(const u32x4*)(qp + 32 * kk);
-        load_coef<D>(g.table, c.rq + cc, gq, qc[w]);
-    }
-    float2 rt[P];
-    {
-        const float2* rp = g.table + (int64_t)kr_t * (D / 2) + kr_i;
-#pragma unroll
-        for (int i = 0; i < P; ++i) rt[i] = rp[i];
-    }
-    // group wg walks visits k0 + wg, k0 + wg + WG, ... (n_mine of them); all
-    // waves run n_steps steps (two block-wide barriers each)
-    const int n_steps = (k1 - k0 + WG - 1) / WG;
-    const int n_mine = k0 + wg < k1 ? (k1 - k0 - wg + WG - 1) / WG : 0;
-    for (int i = 0; i < NBUF - 1; ++i)
-        if (i < n_mine) issue(k0 + wg + WG * i, i);
-
-    // queries rotated once into MFMA B operands (zero for padding rows)
-    bf16x8 qb[NW][KK];
-    int rq_col[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int row = 16 * (wave + 4 * w) + n;
-        rotate_row<D>(qc[w], qr[w], qb[w]);
-        if (row >= rows) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qb[w][kk][e] = (__bf16)0.f;
-        }
-        rq_col[w] = row < rows ? c.rq + row / G : -1;
-    }
-    // column blocks with at least one real row (wave-uniform)
-    const bool act0 = 16 * wave < rows, act1 = NW > 1 && 16 * (wave + 4) < rows;
-
-    floatx4 o[NW][NB];
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int i = 0; i < NB; ++i) o[w][i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m[NW], l[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        m[w] = kNegBig;
-        l[w] = 0.f;
-    }
-    const int r_last = L - 1;
-
-    // One visit with buffer index BF known at compile time (so every LDS
-    // address is a constant offset into lds_buf); the walk runs the steps
-    // 0 .. NBUF-1 in turn.
-    auto step = [&](auto bfc, int si) {
-        constexpr int bf = decltype(bfc)::value;
-        unsigned char* buf = lds_buf + bf * CB::kBytes;
-        const int kv = k0 + wg + WG * si;       // this group's visit (if si < n_mine)
-        const bool mine = si < n_mine;
-        // this wave's loads of the visit have landed once at most the loads of
-        // the group's visits after it (up to NBUF - 2 of them) are outstanding
-        if (mine) wait_visits<CB::nI>(min(NBUF - 2, n_mine - 1 - si));
-        __builtin_amdgcn_s_barrier();          // ... and every wave's; the previous step is done everywhere
-        __builtin_amdgcn_sched_barrier(0);
-        lds_fence();
-        if (si + NBUF - 1 < n_mine) issue(kv + WG * (NBUF - 1), (bf + NBUF - 1) % NBUF);
-
-        // rotate key kr_t (pairs kr_i .. kr_i + P - 1) into the shared tile
-        const int p = visit_tile(c, kv);
-        const int s0 = p * kTile;
-        const int rho = visit_rho(c, kv, s0);
-        const bool seam = (kv == 0) && (c.t_o > 0);
-        if (mine) {
-            // R(rho) pairs kr_i .. as P/2 float4 (16-byte LDS reads)
-            const float4* br = (const float4*)(buf + CB::kK + wave * 1024) + kr_i / 2;
-            const unsigned char* kraw = buf + kr_t * D * 2;
-            float2 cf[P];
-#pragma unroll
-            for (int i2 = 0; i2 < P / 2; ++i2) {
-                const float4 b4 = br[i2];
-                float2 bs[2] = {float2{b4.x, b4.y}, float2{b4.z, b4.w}};
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int i = 2 * i2 + h;
-                    if (kv == 0) bs[h].y = -bs[h].y;                    // R(-t_o)
-                    cf[i] = float2{bs[h].x * rt[i].x - bs[h].y * rt[i].y, bs[h].y * rt[i].x + bs[h].x * rt[i].y};
-                }
-            }
-            if (seam) {                                    // first visit only (wave-uniform)
-                const bool wrap = kr_t < c.t_o;            // index kr_t - t_o + W: R(W) on top
-                const float4* wr = (const float4*)lds_rw + kr_i / 2;
-#pragma unroll
-                for (int i2 = 0; i2 < P / 2; ++i2) {
-                    const float4 w4 = wr[i2];
-                    const float2 w2[2] = {float2{w4.x, w4.y}, float2{w4.z, w4.w}};
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int i = 2 * i2 + h;
-                        const float2 a = cf[i];
-                        const float2 r = {w2[h].x * a.x - w2[h].y * a.y, w2[h].y * a.x + w2[h].x * a.y};
-                        cf[i] = wrap ? r : a;
-                    }
-                }
-            }
-            uint32_t x1w[P / 2], x2w[P / 2];
-            if constexpr (P == 8) {
-                const u32x4 a1 = *(const u32x4*)(kraw + 2 * kr_i), a2 = *(const u32x4*)(kraw + 2 * (kr_i + D / 2));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x1w[i] = a1[i];
-                    x2w[i] = a2[i];
-                }
-            } else {
-                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 a1 = *(const u32x2*)(kraw + 2 * kr_i), a2 = *(const u32x2*)(kraw + 2 * (kr_i + D / 2));
-                x1w[0] = a1[0];
-                x1w[1] = a1[1];
-                x2w[0] = a2[0];
-                x2w[1] = a2[1];
-            }
-            __bf16 y1[P], y2[P];
-#pragma unroll
-            for (int i = 0; i < P; ++i) {
-                const float x1 = (i & 1) ? hi_bf16(x1w[i >> 1]) : lo_bf16(x1w[i >> 1]);
-                const float x2 = (i & 1) ? hi_bf16(x2w[i >> 1]) : lo_bf16(x2w[i >> 1]);
-                y1[i] = (__bf16)(x1 * cf[i].x - x2 * cf[i].y);
-                y2[i] = (__bf16)(x2 * cf[i].x + x1 * cf[i].y);
-            }
-            // dims kr_i .. (16-byte column kr_i / 8) and + D/2 (column + D/16)
-            unsigned char* d1 = lds_kt + 16 * k_pos<D>(kr_t, kr_i / 8) + 2 * (kr_i % 8);
-            unsigned char* d2 = lds_kt + 16 * k_pos<D>(kr_t, (kr_i + D / 2) / 8) + 2 * (kr_i % 8);
-            if constexpr (P == 8) {
-                bf16x8 v1, v2;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    v1[i] = y1[i];
-                    v2[i] = y2[i];
-                }
-                *(bf16x8*)d1 = v1;
-                *(bf16x8*)d2 = v2;
-            } else {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-                bf16x4 v1, v2;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v1[i] = y1[i];
-                    v2[i] = y2[i];
-                }
-                *(bf16x4*)d1 = v1;
-                *(bf16x4*)d2 = v2;
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(kLgkm0);
-        __builtin_amdgcn_s_barrier();          // rotated tile complete
-        __builtin_amdgcn_sched_barrier(0);
-        lds_fence();
-
-        if (!act0 || !mine) return;            // a wave without query rows only helps with the tile
-        bf16x8 kA[2][KK];
-        {
-            const u32x4* kt = (const u32x4*)lds_kt;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                kA[0][kk] = __builtin_bit_cast(bf16x8, kt[k_pos<D>(c.tb0, gq + 4 * kk)]);
-                kA[1][kk] = __builtin_bit_cast(bf16x8, kt[k_pos<D>(c.tb1, gq + 4 * kk)]);
-            }
-        }
-        u32x4 vv[NB];
-        {
-            const u32x4* lb = (const u32x4*)(buf + CB::kK + CB::kC) + lane;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) vv[nb] = lb[nb * 64];
-        }
-        const bool full = (kv != 0) && (rho + kTile <= c.rq + 1) && (s0 + kTile <= W);
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            if (w == 1 && !act1) break;
-            floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[0][kk], qb[w][kk], a0, 0, 0, 0);
-                a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA[1][kk], qb[w][kk], a1, 0, 0, 0);
-            }
-            float s[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s[e] *= c.scale_log2;
-            if (!full) {
-                // branch-free: key index r of each score, then a select
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int tt = 8 * gq + e;
-                    const int r = rho + tt + ((seam & (tt < c.t_o)) ? W : 0);
-                    const bool ok = (r >= 0) & (r <= r_last) & ((rq_col[w] < 0) | (r <= rq_col[w])) & (s0 + tt < W);
-                    s[e] = ok ? s[e] : -INFINITY;
-                }
-            }
-            float mx = s[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const bool grow = mx > m[w] + 8.f;           // lazy rescale, wave-uniform branch
-            if (__any(grow)) {
-                const float mn = grow ? mx : m[w];
-                const float alpha = fast_exp2(m[w] - mn);
-                l[w] *= alpha;
-#pragma unroll
-                for (int i = 0; i < NB; ++i) o[w][i] *= alpha;
-                m[w] = mn;
-            }
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float pe = fast_exp2(s[e] - m[w]);
-                l[w] += pe;
-                pb[e] = (__bf16)pe;
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                o[w][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv[nb]), pb, o[w][nb],
-                                                                   0, 0, 0);
-        }
-    };
-    using std::integral_constant;
-    for (int si = 0; si < n_steps; si += NBUF) {
-        step(integral_constant<int, 0>{}, si);
-        if (si + 1 < n_steps) step(integral_constant<int, (NBUF > 1 ? 1 : 0)>{}, si + 1);
-        if (si + 2 < n_steps) step(integral_constant<int, (NBUF > 2 ? 2 : 0)>{}, si + 2);
-        if constexpr (NBUF > 3) {
-            if (si + 3 < n_steps) step(integral_constant<int, (NBUF > 3 ? 3 : 0)>{}, si + 3);
-        }
-        if constexpr (NBUF > 4) {
-            if (si + 4 < n_steps) step(integral_constant<int, (NBUF > 4 ? 4 : 0)>{}, si + 4);
-            if (si + 5 < n_steps) step(integral_constant<int, (NBUF > 5 ? 5 : 0)>{}, si + 5);
-        }
-        if constexpr (NBUF > 6) {
-            if (si + 6 < n_steps) step(integral_constant<int, (NBUF > 6 ? 6 : 0)>{}, si + 6);
-            if (si + 7 < n_steps) step(integral_constant<int, (NBUF > 7 ? 7 : 0)>{}, si + 7);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-
-    // this block's partial for the wave's rows: O^T element (dim 16 nb + 4 gq + j,
-    // column n) in o[w][nb][j]
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        l[w] += __shfl_xor(l[w], 16);
-        l[w] += __shfl_xor(l[w], 32);
-    }
-    if constexpr (WG == 2) {
-        // group 1 hands its (m, l, O) of every row to group 0 through LDS
-        float* xo = (float*)lds_bufs;                         // [row][D]
-        float* xml = xo + 4 * NW * 16 * D;                    // [row][2]
-        __syncthreads();
-        if (wg == 1) {
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const int lr = 16 * (wave + 4 * w) + n;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    *(float4*)&xo[lr * D + 16 * nb + 4 * gq] = float4{o[w][nb][0], o[w][nb][1], o[w][nb][2], o[w][nb][3]};
-                if (gq == 0) *(float2*)&xml[lr * 2] = float2{m[w], l[w]};
-            }
-        }
-        __syncthreads();
-        if (wg == 1) return;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const int lr = 16 * (wave + 4 * w) + n;
-            const float2 ml1 = *(const float2*)&xml[lr * 2];
-            const float mn = fmaxf(m[w], ml1.x);
-            const float a0 = exp2f(m[w] - mn), a1 = exp2f(ml1.x - mn);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float4 x = *(const float4*)&xo[lr * D + 16 * nb + 4 * gq];
-                o[w][nb][0] = o[w][nb][0] * a0 + x.x * a1;
-                o[w][nb][1] = o[w][nb][1] * a0 + x.y * a1;
-                o[w][nb][2] = o[w][nb][2] * a0 + x.z * a1;
-                o[w][nb][3] = o[w][nb][3] * a0 + x.w * a1;
-            }
-            l[w] = l[w] * a0 + ml1.y * a1;
-            m[w] = mn;
-        }
-    }
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int row = 16 * (wave + 4 * w) + n;
-        if (row >= rows) continue;
-        const int cc = row / G, h = kh * G + (row - cc * G);
-        if (n_split == 1) {
-            const float inv = 1.f / l[w];
-            uint16_t* op = out + (((int64_t)bi * C + cc) * g.hq + h) * D;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) op[16 * nb + 4 * gq + j] = f32_to_bf16_bits(o[w][nb][j] * inv);
-        } else {
-            // partials for combine_kernel (launched next on the same stream)
-            const int64_t pr = part_row(g, bi, kh, split, row);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                *(float4*)&g.part_o[pr * D + 16 * nb + 4 * gq] =
-                    float4{o[w][nb][0], o[w][nb][1], o[w][nb][2], o[w][nb][3]};
-            if (gq == 0) *(float2*)&g.part_ml[pr * 2] = float2{m[w], l[w]};
-        }
-    }
-}
-
-// ---------------------------------------------------------- pipelined chunk --
+//
 // Visit rings of one wave group: K parts (the 32 raw K rows and the visit's
 // R(rho) row) and V parts in separate rings, and two rotated-K tiles.  At step
 // s a group rotates the keys of its visit s + 1 into one tile while it runs
@@ -1962,9 +1149,10 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     unsigned char* const ring_v = gb + PB::dK * PB::kKC;                // dV slots
     unsigned char* const tiles = ring_v + PB::dV * PB::kV;              // 2 rotated tiles
     const int n = lane & 15, gq = lane >> 4;
-    const int bi = blockIdx.z, kh = blockIdx.y, split = blockIdx.x;
+    const int bi = blockIdx.z, kh = blockIdx.y;
+    const int split = blockIdx.x % n_split, row0 = 128 * (blockIdx.x / n_split);
     const int b = st.b0 + bi, G = g.group, W = g.window;
-    const int rows = C * G;
+    const int rows = C * G;                            // rows of this block: row0 + 16 (wave + 4w) + n
 
     DecodeCtx c;
     const int L = st.length[bi];
@@ -2042,7 +1230,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     u32x4 qr[NW][KK];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        int row = 16 * (wave + 4 * w) + n;
+        int row = row0 + 16 * (wave + 4 * w) + n;
         if (row >= rows) row = 0;
         const int cc = row / G, h = kh * G + (row - cc * G);
         const uint16_t* qp = q + (((int64_t)bi * C + cc) * g.hq + h) * D + 8 * gq;
@@ -2051,9 +1239,13 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     }
     float2 rt[P];
     {
-        const float2* rp = g.table + (int64_t)kr_t * (D / 2) + kr_i;
+        const float4* rp = (const float4*)(g.table + (int64_t)kr_t * (D / 2) + kr_i);
 #pragma unroll
-        for (int i = 0; i < P; ++i) rt[i] = rp[i];
+        for (int i = 0; i < P / 2; ++i) {
+            const float4 r4 = rp[i];
+            rt[2 * i] = float2{r4.x, r4.y};
+            rt[2 * i + 1] = float2{r4.z, r4.w};
+        }
     }
     if (wave_b == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
     {
@@ -2067,7 +1259,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     issue_v(0, ring_v);
 
     // column blocks with at least one real row (wave-uniform)
-    const bool act0 = 16 * wave < rows, act1 = NW > 1 && 16 * (wave + 4) < rows;
+    const bool act0 = row0 + 16 * wave < rows, act1 = NW > 1 && row0 + 16 * (wave + 4) < rows;
 
     floatx4 o[NW][NB];
 #pragma unroll
@@ -2167,10 +1359,11 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     };
 
     // Step -1: the rotation of local visit 0 (nothing to compute yet); K(0)
-    // has landed once at most K(1) and V(0) are outstanding.
+    // (and everything issued before it) has landed once at most K(1) and V(0)
+    // are outstanding.
     {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(PB::nK + PB::nV));
-        __builtin_amdgcn_s_barrier();                  // every wave's quarter (and R(W))
+        __builtin_amdgcn_s_barrier();                  // every wave's share
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
         if (n_mine > 2) issue_k(2, ring_k + 2 * PB::kKC);
@@ -2188,7 +1381,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     int rq_col[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        const int row = 16 * (wave + 4 * w) + n;
+        const int row = row0 + 16 * (wave + 4 * w) + n;
         float4 qc[HP][4];
         lds_coef<D>(lds_qc + (row < rows ? row / G : 0) * D * 4, gq, qc);
 #pragma unroll
@@ -2209,10 +1402,11 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     }
 
     // Step s: K(s + 1) and V(s) have landed once at most K(s + 2) and V(s + 1)
-    // (issued by step s - 1, if they exist) are outstanding; after the barrier
-    // every wave is done with step s - 1, so K slot s % 3 (rotated there) and
-    // V slot (s - 1) % 3 (used there) take K(s + 3) and V(s + 2).  Slot and
-    // tile indices repeat every 6 steps; S = s % 6 is a compile-time constant.
+    // (issued by step s - 1, where those visits exist) are outstanding; after
+    // the barrier every wave is done with step s - 1, so K slot s % 3 (rotated
+    // there) and V slot (s - 1) % 3 (used there) take K(s + 3) and V(s + 2).
+    // Slot and tile indices repeat every 6 steps; S = s % 6 is a compile-time
+    // constant.
     auto step = [&](auto sc, int s) {
         constexpr int S = decltype(sc)::value;
         const bool do_r = s + 1 < n_mine, do_c = s < n_mine;
@@ -2365,7 +1559,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     }
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        const int row = 16 * (wave + 4 * w) + n;
+        const int row = row0 + 16 * (wave + 4 * w) + n;
         if (row >= rows) continue;
         const int cc = row / G, h = kh * G + (row - cc * G);
         if (n_split == 1) {
@@ -2387,16 +1581,6 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     }
 }
 
-int env_int(const char* name, int dflt) {
-    const char* s = getenv(name);
-    return s ? atoi(s) : dflt;
-}
-
-int debug_splits() {
-    static const int v = env_int("A8R_DEBUG_SPLITS", -1);
-    return v;
-}
-
 int pick_splits(int pairs, int tiles, int target_blocks, int min_tiles_per_split) {
     int sp = (target_blocks + pairs - 1) / pairs;
     int cap = tiles / min_tiles_per_split;
@@ -2404,7 +1588,6 @@ int pick_splits(int pairs, int tiles, int target_blocks, int min_tiles_per_split
     if (sp > cap) sp = cap;
     if (sp > kMaxSplits) sp = kMaxSplits;
     if (sp < 1) sp = 1;
-    if (debug_splits() > 0) sp = min(debug_splits(), kMaxSplits);
     return sp;
 }
 
@@ -2435,59 +1618,14 @@ hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, 
     return hipGetLastError();
 }
 
-template <int D, int NQ>
-hipError_t run_chunk_mfma(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q, void* out,
-                          int n_cu, hipStream_t s) {
-    const int n_rg = (n_q * g.group + 16 * NQ - 1) / (16 * NQ);
-    const int n_split = pick_splits(st.nb * g.hkv * n_rg, g.w_pad / kTile, n_cu, 4);
-    hipLaunchKernelGGL((chunk_mfma<D, NQ>), dim3(n_split * n_rg, g.hkv, st.nb), dim3(256), 0, s, g, layer, st,
-                       n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
-    return hipGetLastError();
-}
-
-// Up to four 16-row column blocks (64 query rows) per block; larger chunks use
-// several row groups (each re-reads the window).
-template <int D>
-hipError_t run_chunk_mfma_nq(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q,
-                             void* out, int n_cu, hipStream_t s) {
-    const int rows = n_q * g.group;
-    static const int nq_max = env_int("A8R_DEBUG_CHUNK_NQ", 2);   // four blocks spill registers
-    return rows <= 16 || nq_max == 1 ? run_chunk_mfma<D, 1>(g, layer, st, n_q, q, out, n_cu, s)
-         : rows <= 32 || nq_max == 2 ? run_chunk_mfma<D, 2>(g, layer, st, n_q, q, out, n_cu, s)
-                                     : run_chunk_mfma<D, 4>(g, layer, st, n_q, q, out, n_cu, s);
-}
-
 template <int D, int NW>
 hipError_t run_chunk_pipe(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q, void* out,
                           int n_cu, hipStream_t s) {
-    static const int target = env_int("A8R_DEBUG_CHUNK_BLOCKS", 0);
-    static const int groups = env_int("A8R_DEBUG_CHUNK_GROUPS", 2);
-    const int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, target > 0 ? target : n_cu, 4);
-    if (groups == 2)
-        hipLaunchKernelGGL((chunk_pipe<D, NW, 2>), dim3(n_split, g.hkv, st.nb), dim3(512), 0, s, g, layer, st,
-                           n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
-    else
-        hipLaunchKernelGGL((chunk_pipe<D, NW, 1>), dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st,
-                           n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || n_split == 1) return e;
-    // the splits' partials are merged by a second, chip-wide kernel
-    return launch_combine<D, 2>(g, st.nb, n_q, n_split, out, s);
-}
-
-template <int D, int NW>
-hipError_t run_chunk_tiled(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q, void* out,
-                           int n_cu, hipStream_t s) {
-    static const int target = env_int("A8R_DEBUG_CHUNK_BLOCKS", 0);
-    static const int groups = env_int("A8R_DEBUG_CHUNK_GROUPS", 2);
-    const int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, target > 0 ? target : n_cu, 4);
-    // two wave groups (two waves per SIMD) where the registers allow it
-    if (groups == 2)
-        hipLaunchKernelGGL((chunk_tiled<D, NW, 2>), dim3(n_split, g.hkv, st.nb), dim3(512), 0, s, g, layer, st,
-                           n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
-    else
-        hipLaunchKernelGGL((chunk_tiled<D, NW, 1>), dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st,
-                           n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
+    const int n_rg = (n_q * g.group + 127) / 128;      // row groups of up to 128 query rows
+    const int n_split = pick_splits(st.nb * g.hkv * n_rg, g.w_pad / kTile, n_cu, 4);
+    // two wave groups per block: two waves per SIMD
+    hipLaunchKernelGGL((chunk_pipe<D, NW, 2>), dim3(n_split * n_rg, g.hkv, st.nb), dim3(512), 0, s, g, layer, st,
+                       n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split == 1) return e;
     // the splits' partials are merged by a second, chip-wide kernel
@@ -2495,8 +1633,7 @@ hipError_t run_chunk_tiled(const Geometry& g, int layer, const StreamBatch& st, 
 }
 
 bool mfma_chunk_ok(const Geometry& g, int n_q) {
-    return g.elem_bytes == 2 && (g.d == 64 || g.d == 128) && n_q >= 2 && n_q <= kMaxPartialQ &&
-           n_q * g.group <= 32 * kMaxRowGroups;
+    return g.elem_bytes == 2 && (g.d == 64 || g.d == 128) && n_q >= 2 && n_q <= kMaxPartialQ;
 }
 
 }  // namespace
@@ -2524,26 +1661,14 @@ hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now
     if (allow_mfma && n_q == 1 && mfma_decode_ok(g))
         return g.d == 128 ? run_decode_mfma<128>(g, layer, now, q, out, n_cu, nullptr, nullptr, s)
                           : run_decode_mfma<64>(g, layer, now, q, out, n_cu, nullptr, nullptr, s);
-    static const int tiled = env_int("A8R_DEBUG_CHUNK_TILED", 1);
-    if (allow_mfma && mfma_chunk_ok(g, n_q) && tiled == 1) {
-        const bool one = n_q * g.group <= 64;
+    if (allow_mfma && mfma_chunk_ok(g, n_q)) {
+        const bool one = n_q * g.group <= 64;            // one 16-row block per wave suffices
         if (g.d == 128)
             return one ? run_chunk_pipe<128, 1>(g, layer, now, n_q, q, out, n_cu, s)
                        : run_chunk_pipe<128, 2>(g, layer, now, n_q, q, out, n_cu, s);
         return one ? run_chunk_pipe<64, 1>(g, layer, now, n_q, q, out, n_cu, s)
                    : run_chunk_pipe<64, 2>(g, layer, now, n_q, q, out, n_cu, s);
     }
-    if (allow_mfma && mfma_chunk_ok(g, n_q) && tiled == 2) {
-        const bool one = n_q * g.group <= 64;
-        if (g.d == 128)
-            return one ? run_chunk_tiled<128, 1>(g, layer, now, n_q, q, out, n_cu, s)
-                       : run_chunk_tiled<128, 2>(g, layer, now, n_q, q, out, n_cu, s);
-        return one ? run_chunk_tiled<64, 1>(g, layer, now, n_q, q, out, n_cu, s)
-                   : run_chunk_tiled<64, 2>(g, layer, now, n_q, q, out, n_cu, s);
-    }
-    if (allow_mfma && mfma_chunk_ok(g, n_q))
-        return g.d == 128 ? run_chunk_mfma_nq<128>(g, layer, now, n_q, q, out, n_cu, s)
-                          : run_chunk_mfma_nq<64>(g, layer, now, n_q, q, out, n_cu, s);
     int sp = 1;
     if (n_q <= kMaxPartialQ) {
         const int n_rg = (n_q * g.group + 63) / 64;
