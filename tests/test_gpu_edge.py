@@ -90,6 +90,7 @@ def test_fused_append_decode_wraps(window, hq, hkv, d, bf16, portable):
     (64, 8, 16, 2, 128, True), (37, 5, 8, 8, 64, True), (16, 16, 16, 2, 128, True),
     (50, 3, 4, 2, 64, False), (128, 8, 16, 2, 128, True),
     (64, 16, 32, 2, 128, True), (40, 12, 16, 1, 64, True),     # 256 and 192 query rows per KV head
+    (512, 8, 16, 2, 128, True), (1000, 16, 32, 2, 64, True),   # several key splits (merged in the kernel)
 ])
 def test_chunk_stream(window, chunk, hq, hkv, d, bf16, portable):
     say("chunk_stream", window, chunk, hq, hkv, d, bf16, portable)
