@@ -67,10 +67,32 @@ typedef enum a8r_status {
 typedef enum a8r_dtype { A8R_F32 = 0, A8R_BF16 = 1 } a8r_dtype;
 
 /* Kernel selection.  AUTO picks the bf16 MFMA kernels where the shape allows
- * (bf16, head_dim 64 or 128, <= 16 query heads per KV head for decode and
- * <= 64 (queries x group) rows for chunks) and the portable kernels otherwise;
- * PORTABLE forces the portable kernels (used to cross-check the two). */
+ * (bf16, head_dim 64 or 128; decode with <= 16 query heads per KV head; chunks
+ * of 2..16 positions) and the portable kernels otherwise; PORTABLE forces the
+ * portable kernels (used to cross-check the two). */
 typedef enum a8r_kernel_policy { A8R_KERNELS_AUTO = 0, A8R_KERNELS_PORTABLE = 1 } a8r_kernel_policy;
+
+/* How stored keys carry their rotation.
+ *
+ * A8R_ROTATE_ON_READ (the method): K is stored exactly as appended and every
+ * read rotates it by its re-based index ("Audio8 ASR Infinite: What It Actually
+ * Takes to Listen Forever", section "Inside the Rolling KV Cache and Exact RoPE
+ * Re-Basing": re-basing every surviving key to the new origin keeps relative
+ * distances exact).  Stored bits never change, so nothing accumulates.
+ *
+ * A8R_REBASE_ON_EVICT (a comparison variant: the hazard the same page raises
+ * there and in "Failure Modes That Only Appear on Day Three of a Session",
+ * rounding error entering the rotation at every boundary): K is stored already
+ * rotated to its re-based index, in the cache dtype, and whenever an append
+ * evicts e tokens (the origin moves by e) every surviving key is re-rotated by
+ * R(-e) and rounded back to the cache dtype.  Each re-rotation adds rounding
+ * error that never leaves; it also reads and writes the whole K window at every
+ * eviction.  The rotation arithmetic is float32 multiplies and adds without
+ * fusion, rounded once to the cache dtype (round to nearest even).
+ * Decode and chunk attention then use the stored keys as they are (the query is
+ * still rotated by its re-based index).  The fused append + decode call runs as
+ * the two separate steps in this mode. */
+typedef enum a8r_cache_mode { A8R_ROTATE_ON_READ = 0, A8R_REBASE_ON_EVICT = 1 } a8r_cache_mode;
 
 typedef struct a8r_config {
     int32_t n_layers;      /* >= 1 */
@@ -82,7 +104,7 @@ typedef struct a8r_config {
     int32_t max_chunk;     /* 1 <= max_chunk <= W: most tokens per append / chunk call */
     int32_t dtype;         /* a8r_dtype */
     int32_t kernel_policy; /* a8r_kernel_policy */
-    int32_t reserved;      /* must be 0 */
+    int32_t cache_mode;    /* a8r_cache_mode (0 = A8R_ROTATE_ON_READ) */
     double rope_theta;     /* > 0; frequencies theta^(-2i/head_dim), split-half pairs (i, i + head_dim/2) */
     float softmax_scale;   /* > 0, or <= 0 for 1/sqrt(head_dim) */
     float reserved_f;      /* must be 0 */
@@ -180,7 +202,8 @@ a8r_status a8r_append_decode_attn(a8r_cache* cache, int32_t layer, int32_t b0, i
 a8r_status a8r_get_state(a8r_cache* cache, int32_t layer, int32_t b, int64_t* next_pos,
                          int32_t* length, int32_t* next_slot);
 
-/* Copy the raw ring of one (layer, stream) pair to host, in physical slot order:
+/* Copy the raw ring of one (layer, stream) pair to host, in physical slot order
+ * (with A8R_REBASE_ON_EVICT the K ring holds the rotated keys):
  * k_host, v_host: host [W][n_kv_heads][head_dim] dtype elements (either may be
  * NULL).  Synchronizes the stream.  For tests and tooling. */
 a8r_status a8r_read_ring(a8r_cache* cache, int32_t layer, int32_t b, void* k_host, void* v_host);

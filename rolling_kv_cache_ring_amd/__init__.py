@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "liba8r.so")
 A8R_OK, A8R_EINVAL, A8R_ENOMEM, A8R_EDEVICE, A8R_ESTATE, A8R_EUNSUPPORTED = range(6)
 A8R_F32, A8R_BF16 = 0, 1
 A8R_KERNELS_AUTO, A8R_KERNELS_PORTABLE = 0, 1
+A8R_ROTATE_ON_READ, A8R_REBASE_ON_EVICT = 0, 1
 STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ENOMEM", 3: "EDEVICE", 4: "ESTATE", 5: "EUNSUPPORTED"}
 
 EXPORTED = [
@@ -51,7 +52,7 @@ class Config(ctypes.Structure):
         ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
         ("max_chunk", ctypes.c_int32), ("dtype", ctypes.c_int32),
-        ("kernel_policy", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("kernel_policy", ctypes.c_int32), ("cache_mode", ctypes.c_int32),
         ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
         ("reserved_f", ctypes.c_float),
     ]
@@ -147,10 +148,12 @@ def _i32_array(vals):
 
 
 def make_config(n_layers, n_streams, n_q_heads, n_kv_heads, head_dim, window, max_chunk=1,
-                bf16=True, rope_theta=1.0e6, softmax_scale=0.0, portable=False) -> Config:
+                bf16=True, rope_theta=1.0e6, softmax_scale=0.0, portable=False,
+                rebase_on_evict=False) -> Config:
     return Config(n_layers, n_streams, n_q_heads, n_kv_heads, head_dim, window, max_chunk,
                   A8R_BF16 if bf16 else A8R_F32,
-                  A8R_KERNELS_PORTABLE if portable else A8R_KERNELS_AUTO, 0,
+                  A8R_KERNELS_PORTABLE if portable else A8R_KERNELS_AUTO,
+                  A8R_REBASE_ON_EVICT if rebase_on_evict else A8R_ROTATE_ON_READ,
                   float(rope_theta), float(softmax_scale), 0.0)
 
 

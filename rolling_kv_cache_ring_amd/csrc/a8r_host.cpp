@@ -139,7 +139,9 @@ a8r_status validate_config(const a8r_config* c) {
     if (c->dtype != A8R_F32 && c->dtype != A8R_BF16) return fail(A8R_EINVAL, "dtype %d", c->dtype);
     if (c->kernel_policy != A8R_KERNELS_AUTO && c->kernel_policy != A8R_KERNELS_PORTABLE)
         return fail(A8R_EINVAL, "kernel_policy %d", c->kernel_policy);
-    if (c->reserved != 0 || c->reserved_f != 0.f) return fail(A8R_EINVAL, "reserved fields must be 0");
+    if (c->cache_mode != A8R_ROTATE_ON_READ && c->cache_mode != A8R_REBASE_ON_EVICT)
+        return fail(A8R_EINVAL, "cache_mode %d", c->cache_mode);
+    if (c->reserved_f != 0.f) return fail(A8R_EINVAL, "reserved_f must be 0");
     if (!(c->rope_theta > 0.0) || !isfinite(c->rope_theta)) return fail(A8R_EINVAL, "rope_theta must be > 0");
     if (!isfinite(c->softmax_scale)) return fail(A8R_EINVAL, "softmax_scale must be finite");
     if ((int64_t)c->n_q_heads * (int64_t)c->n_streams > (1 << 24))
@@ -327,6 +329,7 @@ a8r_status a8r_cache_create(const a8r_config* cfg, void* hip_stream, void* works
     g.window = cfg->window;
     g.w_pad = lay.w_pad;
     g.elem_bytes = cfg->dtype == A8R_BF16 ? 2 : 4;
+    g.prerot = cfg->cache_mode == A8R_REBASE_ON_EVICT;
     g.rows_max = lay.rows_max;
     const double scale = cfg->softmax_scale > 0.f ? (double)cfg->softmax_scale : 1.0 / sqrt((double)cfg->head_dim);
     g.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
@@ -416,6 +419,7 @@ a8r_status a8r_append_kv(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, in
         fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
         hipError_t e = a8r::launch_append(c->geo, layer, sb, n_new, (const uint8_t*)k + i0 * row,
                                           (const uint8_t*)v + i0 * row, c->stream);
+        if (e == hipSuccess && c->geo.prerot) e = a8r::launch_rebase(c->geo, layer, sb, n_new, c->stream);
         if (e != hipSuccess) return device_fail(c, e, "append kernel");
     }
     c->ledger.append(layer, b0, nb, n_new, slots_out, evicted_out);

@@ -66,6 +66,7 @@ struct Geometry {
                         // [n_streams][n_kv_heads][kMaxGroupTagged][D], kSlotEmpty between calls
     int n_layers, n_streams, hq, hkv, group, d, window, w_pad;
     int elem_bytes;     // 2 (bf16) or 4 (f32)
+    int prerot;         // keys are stored rotated to their re-based index (A8R_REBASE_ON_EVICT)
     int rows_max;       // max(1, min(max_chunk, kMaxPartialQ)) * group
     float scale_log2;   // softmax scale * log2(e): scores are kept in base-2 units
 };
@@ -80,6 +81,10 @@ __host__ __device__ inline int64_t pair_index(const Geometry& g, int layer, int 
 // Device pointers k, v, q, out point at the batch's first stream.
 // Writes the device state record of every layer for a batch of reset streams.
 hipError_t launch_reset(const Geometry& g, const StreamBatch& after, hipStream_t s);
+// A8R_REBASE_ON_EVICT, after launch_append of n tokens (state `before` the
+// append): rotates the new tokens' keys to their re-based indices and, where
+// the append evicted e tokens, every surviving key by R(-e), in place.
+hipError_t launch_rebase(const Geometry& g, int layer, const StreamBatch& before, int n, hipStream_t s);
 // Copies n_new tokens per stream into the ring; `before` is the state before.
 hipError_t launch_append(const Geometry& g, int layer, const StreamBatch& before, int n_new,
                          const void* k, const void* v, hipStream_t s);

@@ -152,6 +152,44 @@ __global__ __launch_bounds__(256) void append_kernel(Geometry g, int layer, Stre
     }
 }
 
+// ------------------------------------------------------ rebase on evict ----
+// A8R_REBASE_ON_EVICT (a comparison variant): keys are stored rotated to their
+// re-based index.  After an append of n tokens to a window of L0 keys (state
+// `before`), the window holds L1 = min(L0 + n, W) keys and its origin moved by
+// e = L0 + n - L1: the new tokens (indices L1 - n .. L1 - 1, written unrotated
+// by append_kernel) are rotated by R(r), and every surviving key by
+// R(-e) = R(e) conjugated.  Each pair is computed with float32 multiplies and
+// adds without fusion and rounded once to the cache dtype, so the rounding of
+// every re-rotation stays in the stored key.  Block = (256 keys of the window,
+// KV head, stream); a thread takes one pair (i, i + D/2) of one key.
+template <int D, int EB>
+__global__ __launch_bounds__(256) void rebase_kernel(Geometry g, int layer, StreamBatch before, int n) {
+    constexpr int NP = D / 2;
+    const int bi = blockIdx.z, kh = blockIdx.y, r0 = blockIdx.x * 256;
+    const int b = before.b0 + bi, W = g.window;
+    const int L0 = before.length[bi];
+    const int L1 = min(L0 + n, W), e = L0 + n - L1;
+    int oldest = (before.next_slot[bi] + n - L1) % W;  // in (-W, W)
+    if (oldest < 0) oldest += W;
+    const int r_new = L1 - n;
+    const int r_begin = e > 0 ? r0 : max(r0, r_new);   // without an eviction only new keys change
+    const int r_end = min(r0 + 256, L1);
+    if (r_begin >= r_end) return;
+    uint8_t* kring = (uint8_t*)g.k_ring + pair_index(g, layer, b, kh) * g.w_pad * D * EB;
+    const int cnt = (r_end - r_begin) * NP;
+    for (int t = threadIdx.x; t < cnt; t += 256) {
+#pragma clang fp contract(off)
+        const int r = r_begin + t / NP, i = t % NP;
+        const int64_t at = (int64_t)wrap_slot(oldest + r, W) * D + i;
+        float2 cs = g.table[(int64_t)(r >= r_new ? r : e) * NP + i];
+        if (r < r_new) cs.y = -cs.y;
+        const float x1 = load_elem<EB>(kring, at), x2 = load_elem<EB>(kring, at + NP);
+        const float a = x1 * cs.x, b2 = x2 * cs.y, c2 = x2 * cs.x, d2 = x1 * cs.y;
+        store_elem<EB>(kring, at, a - b2);
+        store_elem<EB>(kring, at + NP, c2 + d2);
+    }
+}
+
 // ------------------------------------------------------ split partials ----
 __device__ __forceinline__ int64_t part_row(const Geometry& g, int bi, int kh, int split, int row) {
     return (((int64_t)bi * g.hkv + kh) * kMaxSplits + split) * g.rows_max + row;
@@ -282,7 +320,8 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
                 const int slot = wrap_slot(oldest + r, W);
                 const float x1 = load_elem<EB>(kring, (int64_t)slot * D + i);
                 const float x2 = load_elem<EB>(kring, (int64_t)slot * D + i + NP);
-                const float2 cs = g.table[(int64_t)r * NP + i];
+                // keys stored already rotated (A8R_REBASE_ON_EVICT) are used as they are
+                const float2 cs = g.prerot ? float2{1.f, 0.f} : g.table[(int64_t)r * NP + i];
                 k1 = x1 * cs.x - x2 * cs.y;
                 k2 = x2 * cs.x + x1 * cs.y;
                 const int64_t vb = (int64_t)(slot >> 3) * D * 8 + (slot & 7);
@@ -399,6 +438,7 @@ struct DecodeCtx {
     const uint16_t* vp;
     const float2* table;
     int oldest, t_o, p0t, n_tiles, L, W, rq, tb0, tb1, gq, n;
+    int prerot;        // keys stored rotated to their index: only the query is rotated
     float scale_log2;
 };
 
@@ -528,7 +568,8 @@ __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, 
         dma16(c.kp + (int64_t)(s0 + r) * D + 8 * col, kbuf + j * 1024);
     }
     const int rho = visit_rho(c, k, s0);
-    dma_table_row<D>(c.table, CHUNK ? (rho < 0 ? -rho : rho) : c.rq - rho, lane, kbuf + 2 * (D / 32) * 1024);
+    dma_table_row<D>(c.table, CHUNK ? (rho < 0 ? -rho : rho) : c.rq - (c.prerot ? 0 : rho), lane,
+                     kbuf + 2 * (D / 32) * 1024);
 }
 
 template <int D>
@@ -727,6 +768,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     c.gq = gq;
     c.n = n;
     c.scale_log2 = g.scale_log2;
+    c.prerot = g.prerot;
     c.table = g.table;
     const int64_t pair = pair_index(g, layer, b, kh);
     c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
@@ -810,6 +852,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         for (int kk = 0; kk < KK; ++kk) qraw[kk] = *(const u32x4*)(qrow + 64 * kk);
         lds_coef<D>(lds_rt + c.tb0 * D * 4, gq, cf0);
         lds_coef<D>(lds_rt + c.tb1 * D * 4, gq, cf1);
+        if (c.prerot) {                  // keys already rotated: R(t) is the identity
+#pragma unroll
+            for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cf0[kk][j] = cf1[kk][j] = float4{1.f, 0.f, 1.f, 0.f};
+        }
     }
 
     floatx4 o[NB];
@@ -846,7 +894,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         __builtin_amdgcn_s_waitcnt(kLgkm0);                                 // copied out of ka
         if (k + 8 < k1) dec_load_k<D>(c, k + 8, lane, ka);
         bf16x8 pb;
-        if (k == 0 && c.t_o > 0) {      // the seam visit (a wave-uniform branch)
+        if (k == 0 && c.t_o > 0 && !c.prerot) {   // the seam visit (a wave-uniform branch)
             float4 rw[D / 64][4], s0c[D / 64][4], s1c[D / 64][4];
             lds_coef<D>(lds_rw, gq, rw);
             seam_coef<D>(rw, cf0, c.tb0 < c.t_o, s0c);
@@ -1168,6 +1216,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     c.gq = gq;
     c.n = n;
     c.scale_log2 = g.scale_log2;
+    c.prerot = 0;
     c.table = g.table;
     const int64_t pair = pair_index(g, layer, b, kh);
     c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
@@ -1661,7 +1710,7 @@ hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now
     if (allow_mfma && n_q == 1 && mfma_decode_ok(g))
         return g.d == 128 ? run_decode_mfma<128>(g, layer, now, q, out, n_cu, nullptr, nullptr, s)
                           : run_decode_mfma<64>(g, layer, now, q, out, n_cu, nullptr, nullptr, s);
-    if (allow_mfma && mfma_chunk_ok(g, n_q)) {
+    if (allow_mfma && mfma_chunk_ok(g, n_q) && !g.prerot) {
         const bool one = n_q * g.group <= 64;            // one 16-row block per wave suffices
         if (g.d == 128)
             return one ? run_chunk_pipe<128, 1>(g, layer, now, n_q, q, out, n_cu, s)
@@ -1681,13 +1730,26 @@ hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now
                       : run_portable<64, 4>(g, layer, now, n_q, q, out, sp, s);
 }
 
+hipError_t launch_rebase(const Geometry& g, int layer, const StreamBatch& before, int n, hipStream_t s) {
+    const dim3 grid((g.window + 255) / 256, g.hkv, before.nb);
+    if (g.elem_bytes == 2) {
+        if (g.d == 128) hipLaunchKernelGGL((rebase_kernel<128, 2>), grid, dim3(256), 0, s, g, layer, before, n);
+        else hipLaunchKernelGGL((rebase_kernel<64, 2>), grid, dim3(256), 0, s, g, layer, before, n);
+    } else {
+        if (g.d == 128) hipLaunchKernelGGL((rebase_kernel<128, 4>), grid, dim3(256), 0, s, g, layer, before, n);
+        else hipLaunchKernelGGL((rebase_kernel<64, 4>), grid, dim3(256), 0, s, g, layer, before, n);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_append_decode(const Geometry& g, int layer, const StreamBatch& before, const void* k,
                                 const void* v, const void* q, void* out, bool allow_mfma, int n_cu,
                                 hipStream_t s) {
-    if (allow_mfma && mfma_decode_ok(g))
+    if (allow_mfma && mfma_decode_ok(g) && !g.prerot)
         return g.d == 128 ? run_decode_mfma<128>(g, layer, before, q, out, n_cu, k, v, s)
                           : run_decode_mfma<64>(g, layer, before, q, out, n_cu, k, v, s);
     hipError_t e = launch_append(g, layer, before, 1, k, v, s);
+    if (e == hipSuccess && g.prerot) e = launch_rebase(g, layer, before, 1, s);
     if (e != hipSuccess) return e;
     StreamBatch now = before;
     for (int i = 0; i < now.nb; ++i) {
