@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
                     help="decode step per layer as one a8r_append_decode_attn call (fused) or as "
                          "a8r_append_kv + a8r_decode_attn (separate)")
+    ap.add_argument("--cache-mode", default="rotate_on_read", choices=["rotate_on_read", "rebase_on_evict"],
+                    help="rebase_on_evict runs the comparison variant (keys stored rotated and re-rotated at "
+                         "every eviction); the fused call then runs as append + decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -240,7 +243,8 @@ def main():
     B, NL, hq, hkv, d, w, c = (wl.n_streams, wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
                                wl.window, wl.chunk)
     stream = torch.cuda.current_stream()
-    cfg = a8r.make_config(NL, B, hq, hkv, d, w, w, True)
+    rebase = args.cache_mode == "rebase_on_evict"
+    cfg = a8r.make_config(NL, B, hq, hkv, d, w, w, True, rebase_on_evict=rebase)
     cache = a8r.Cache(cfg, stream=stream.cuda_stream)
 
     # seeded start states; pre-fill each stream to min(P0, W) tokens ending at P0 - 1
@@ -273,7 +277,7 @@ def main():
     h = cache.handle
     L = a8r.lib()
 
-    fused = c == 1 and args.path == "fused"
+    fused = c == 1 and args.path == "fused" and not rebase
 
     def check(st):
         if st:
@@ -364,7 +368,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "path": "fused" if fused else "separate", "layers": NL, "streams": B, "q_heads": hq, "kv_heads": hkv,
+        "config": {"workload": wl.name, "path": "fused" if fused else "separate",
+                   "cache_mode": args.cache_mode, "layers": NL, "streams": B, "q_heads": hq, "kv_heads": hkv,
                    "head_dim": d, "window": w, "positions_per_step": c,
                    "start_positions": "seeded U[0,1e6)" if c == 1 else "seeded U[2^24-W,2^24)"},
         "kv_gbps": round(gbps_step, 1),
@@ -388,6 +393,13 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
+    if rebase:
+        # the variant's extra work: every eviction re-rotates the whole K window
+        # (read + write), per layer and step at full windows
+        line["rebase"] = {
+            "k_bytes_per_layer": B * hkv * w * d * 2 * 2,
+            "append_and_rebase_ms_per_layer": round(ms / NL - attn_ms, 5),
+        }
     print(json.dumps(line), flush=True)
     cache.close()
 

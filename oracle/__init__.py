@@ -26,9 +26,11 @@ rope       -- split-half rotary embedding at a given (re-based) index.
 attention  -- re-based decode / chunk attention over the live window, and the
               brute-force attention at absolute positions it must equal.
 model      -- a whole cache (layers x streams) built from the three above.
+rebase     -- the rebase-on-evict comparison variant (keys stored rotated and
+              re-rotated at every eviction, its float32/bf16 rounding emulated).
 
 Parity status of every function is pinned by tests under ``tests/`` marked
 ``not gpu``; none is "parity unpinned".
 """
 
-from . import ledger, rope, attention, model  # noqa: F401
+from . import ledger, rope, attention, model, rebase  # noqa: F401
