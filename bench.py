@@ -11,7 +11,8 @@ through).  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps 1000] [--warmup 20] [--workload qwen3b_batch64]
 
-``--workload qwen3b_chunk8`` measures the 8-position chunk path instead.
+``--workload qwen3b_chunk8`` measures the 8-position chunk path instead;
+``--prefix F`` pins an F-token prompt prefix in every (layer, stream) first.
 """
 
 from __future__ import annotations
@@ -48,6 +49,9 @@ def parse():
     ap.add_argument("--cache-mode", default="rotate_on_read", choices=["rotate_on_read", "rebase_on_evict"],
                     help="rebase_on_evict runs the comparison variant (keys stored rotated and re-rotated at "
                          "every eviction); the fused call then runs as append + decode")
+    ap.add_argument("--prefix", type=int, default=0, metavar="F",
+                    help="pin an F-token prompt prefix in every (layer, stream) before the pre-fill; "
+                         "attention then covers F + W keys")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -123,7 +127,7 @@ def summarize(args):
             rec = json.load(open(rec_path))
         except (OSError, ValueError):
             rec = {}
-        wl = args.workload
+        wl = args.workload + (f"+prefix{args.prefix}" if args.prefix else "")
         entry = rec.get(wl, {})
         if entry.get("kernel_sha256_16") != kernel_hash():
             entry = {}      # counters taken on an older kernel source no longer apply
@@ -244,7 +248,8 @@ def main():
                                wl.window, wl.chunk)
     stream = torch.cuda.current_stream()
     rebase = args.cache_mode == "rebase_on_evict"
-    cfg = a8r.make_config(NL, B, hq, hkv, d, w, w, True, rebase_on_evict=rebase)
+    F = args.prefix
+    cfg = a8r.make_config(NL, B, hq, hkv, d, w, w, True, rebase_on_evict=rebase, prefix_capacity=F)
     cache = a8r.Cache(cfg, stream=stream.cuda_stream)
 
     # seeded start states; pre-fill each stream to min(P0, W) tokens ending at P0 - 1
@@ -254,6 +259,12 @@ def main():
     gen = torch.Generator(device="cuda")
     gen.manual_seed(0xA8)
     bf = torch.bfloat16
+    if F:
+        for layer in range(NL):
+            pk = torch.randn((B, F, hkv, d), device="cuda", generator=gen).to(bf).view(torch.int16)
+            pv = torch.randn((B, F, hkv, d), device="cuda", generator=gen).to(bf).view(torch.int16)
+            cache.append_prefix(layer, 0, B, F, pk, pv)
+        del pk, pv
     fill = torch.randn((B, w, hkv, d), device="cuda", generator=gen).to(bf).view(torch.int16)
     fill_v = torch.randn((B, w, hkv, d), device="cuda", generator=gen).to(bf).view(torch.int16)
     for layer in range(NL):
@@ -340,13 +351,13 @@ def main():
         n_launch = n_t * NL
         attn_ms = a0.elapsed_time(a1) / n_launch
 
-    live = w  # every stream holds a full window after pre-fill
+    live = w + F  # every stream holds a full window after pre-fill, after its prefix
     bytes_launch = algorithmic_bytes(wl, live)
     bytes_step = NL * (bytes_launch + append_bytes(wl))
     gbps_step = bytes_step * steps_per_s / 1e9
     achieved = bytes_launch / (attn_ms * 1e-3) / 1e9
     flops_launch = attention_flops(wl, live)
-    traffic = traffic_from_profiles(args.workload)
+    traffic = traffic_from_profiles(args.workload + (f"+prefix{F}" if F else ""))
 
     if args.copy_probe:
         copy_probe(torch)
@@ -370,7 +381,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "path": "fused" if fused else "separate",
                    "cache_mode": args.cache_mode, "layers": NL, "streams": B, "q_heads": hq, "kv_heads": hkv,
-                   "head_dim": d, "window": w, "positions_per_step": c,
+                   "head_dim": d, "window": w, "positions_per_step": c, "prefix": F,
                    "start_positions": "seeded U[0,1e6)" if c == 1 else "seeded U[2^24-W,2^24)"},
         "kv_gbps": round(gbps_step, 1),
         "hbm_frac_step": round(gbps_step / HBM_PEAK_GBPS, 4),

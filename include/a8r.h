@@ -108,6 +108,9 @@ typedef struct a8r_config {
     double rope_theta;     /* > 0; frequencies theta^(-2i/head_dim), split-half pairs (i, i + head_dim/2) */
     float softmax_scale;   /* > 0, or <= 0 for 1/sqrt(head_dim) */
     float reserved_f;      /* must be 0 */
+    int32_t prefix_capacity; /* >= 0: pinned prefix tokens per (layer, stream) besides the W ring
+                                (see a8r_append_prefix); 0 = none */
+    int32_t reserved;      /* must be 0 */
 } a8r_config;
 
 typedef struct a8r_cache a8r_cache;
@@ -143,6 +146,41 @@ a8r_status a8r_set_stream(a8r_cache* cache, void* hip_stream);
  * Errors: EINVAL, ESTATE (poisoned), EDEVICE. */
 a8r_status a8r_reset(a8r_cache* cache, int32_t b0, int32_t nb, const int64_t* next_pos,
                      const int32_t* next_slot);
+
+/* Pinned prompt prefix.  A stream may hold up to prefix_capacity prefix tokens
+ * that are never evicted, besides its W-token ring ("Audio8-ASR-Infinite-
+ * Compressed", Linux CPU notes: an audio-independent prompt prefix prepared
+ * once and re-checked at every silence reset).  The pages do not say how a
+ * pinned prefix meets re-basing; the reading here: attention runs over the
+ * sequence [prefix; live window] with consecutive re-based indices, so prefix
+ * token j has index j, the window's live tokens F .. F + L - 1 (F = prefix
+ * length), and a chunk's query c index F + L - C + c.  The prefix-to-query
+ * distance therefore grows while the window fills and then stays fixed, like
+ * every other distance in the window.
+ *
+ * a8r_append_prefix appends n_new tokens to the prefix of streams [b0, b0+nb)
+ * in one layer.  k, v: device [nb][n_new][n_kv_heads][head_dim], 16-byte
+ * aligned.  The stream's ring in that layer must be empty (L == 0: the prefix
+ * precedes the window) and F + n_new <= prefix_capacity.  a8r_reset leaves
+ * prefixes in place; a8r_clear_prefix empties them in every layer.  Not
+ * available with A8R_REBASE_ON_EVICT (EUNSUPPORTED).
+ * Errors: EINVAL, ESTATE (ring not empty, poisoned), EUNSUPPORTED, EDEVICE. */
+a8r_status a8r_append_prefix(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb, int32_t n_new,
+                             const void* k, const void* v);
+/* Export of a prepared prefix (the pages prepare a prefix once, as a separate
+ * operation, and load it for every session; "Audio8-ASR-Infinite-Compressed",
+ * Linux CPU notes).  Copies the n prefix tokens of streams [b0, b0+nb) in one
+ * layer to k_out, v_out: device [nb][n][n_kv_heads][head_dim], 16-byte aligned,
+ * the layout a8r_append_prefix takes, bit for bit as appended (so appending
+ * them to another cache of the same shape and dtype imports the prefix).
+ * Every stream in the range must hold exactly n >= 1 prefix tokens.
+ * Asynchronous on the cache's stream.  Errors: EINVAL, ESTATE (poisoned),
+ * EDEVICE. */
+a8r_status a8r_export_prefix(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb, int32_t n,
+                             void* k_out, void* v_out);
+a8r_status a8r_clear_prefix(a8r_cache* cache, int32_t b0, int32_t nb);
+/* Prefix length F of one (layer, stream) pair (host output). */
+a8r_status a8r_prefix_length(a8r_cache* cache, int32_t layer, int32_t b, int32_t* length);
 
 /* Append n_new tokens to streams [b0, b0 + nb) of one layer.  k, v: device,
  * [nb][n_new][n_kv_heads][head_dim], dtype elements.  Token j of stream b takes

@@ -16,6 +16,14 @@ Re-Basing" (fixed capacity, oldest-first eviction, re-based indices), plus the
 reset after a completed utterance shown by the flowchart's node "Emit final
 segment, reset utterance state".  The reset applies to every layer of a stream.
 
+A pinned prompt prefix (the pages mention an audio-independent prompt prefix
+prepared once and re-checked at every silence reset, "Audio8-ASR-Infinite-
+Compressed", Linux CPU notes; they do not say how it meets re-basing) is kept
+per pair outside the ring and never evicted.  Reading: attention runs over the
+sequence [prefix; live window] with consecutive re-based indices, i.e. exactly
+the method's re-based attention over that concatenation.  A reset leaves the
+prefix in place; ``clear_prefix`` empties it.
+
 Pairs are materialised lazily, so a test can follow a few (layer, stream) pairs
 of a very large configuration.
 """
@@ -40,6 +48,7 @@ class OracleCache:
         self.theta, self.scale = theta, scale
         self._start = [(0, 0) for _ in range(n_streams)]      # (next_pos, next_slot) at reset
         self._pairs: dict[tuple[int, int], tuple[StreamLedger, np.ndarray, np.ndarray]] = {}
+        self._prefix: dict[tuple[int, int], tuple[np.ndarray, np.ndarray]] = {}
 
     # -- storage -----------------------------------------------------------
     def _pair(self, layer: int, b: int):
@@ -81,6 +90,24 @@ class OracleCache:
             evicted.append(e)
         return slots, evicted
 
+    def append_prefix(self, layer: int, b0: int, k: np.ndarray, v: np.ndarray) -> None:
+        """Pin k, v [nb, n_new, Hkv, D] after each stream's prefix (its window must be empty)."""
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        for i in range(k.shape[0]):
+            if self._pair(layer, b0 + i)[0].length:
+                raise RuntimeError("the prefix must precede the window")
+            pk, pv = self.prefix_kv(layer, b0 + i)
+            self._prefix[(layer, b0 + i)] = (np.concatenate([pk, k[i]]), np.concatenate([pv, v[i]]))
+
+    def clear_prefix(self, b0: int, nb: int) -> None:
+        for key in [key for key in self._prefix if b0 <= key[1] < b0 + nb]:
+            del self._prefix[key]
+
+    def prefix_kv(self, layer: int, b: int):
+        empty = np.zeros((0, self.hkv, self.d), dtype=np.float64)
+        return self._prefix.get((layer, b), (empty, empty))
+
     def window_kv(self, layer: int, b: int):
         """Live keys and values oldest first, [L, Hkv, D] each, and the origin."""
         led, ring_k, ring_v = self._pair(layer, b)
@@ -95,7 +122,9 @@ class OracleCache:
             kw, vw, _ = self.window_kv(layer, b0 + i)
             if kw.shape[0] == 0:
                 raise RuntimeError("attention over an empty window")
-            out[i] = chunk_rebased(q[i], kw, vw, self.theta, self.scale)
+            pk, pv = self.prefix_kv(layer, b0 + i)
+            out[i] = chunk_rebased(q[i], np.concatenate([pk, kw]), np.concatenate([pv, vw]), self.theta,
+                                   self.scale)
         return out
 
     def decode(self, layer: int, b0: int, q: np.ndarray) -> np.ndarray:

@@ -30,7 +30,8 @@ STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ENOMEM", 3: "EDEVICE", 4: "ESTATE", 5:
 EXPORTED = [
     "a8r_workspace_bytes", "a8r_cache_create", "a8r_cache_destroy", "a8r_set_stream", "a8r_reset",
     "a8r_append_kv", "a8r_decode_attn", "a8r_chunk_attn", "a8r_append_decode_attn",
-    "a8r_get_state", "a8r_read_ring",
+    "a8r_get_state", "a8r_read_ring", "a8r_append_prefix", "a8r_export_prefix", "a8r_clear_prefix",
+    "a8r_prefix_length",
     "a8r_last_error", "a8r_ledger_create", "a8r_ledger_destroy", "a8r_ledger_reset",
     "a8r_ledger_append", "a8r_ledger_get", "a8r_version",
 ]
@@ -54,7 +55,7 @@ class Config(ctypes.Structure):
         ("max_chunk", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("kernel_policy", ctypes.c_int32), ("cache_mode", ctypes.c_int32),
         ("rope_theta", ctypes.c_double), ("softmax_scale", ctypes.c_float),
-        ("reserved_f", ctypes.c_float),
+        ("reserved_f", ctypes.c_float), ("prefix_capacity", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -96,6 +97,16 @@ def lib():
     L.a8r_append_decode_attn.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32p, _i64p]
     L.a8r_append_decode_attn.restype = st
+    L.a8r_append_prefix.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    _c_void_p, _c_void_p]
+    L.a8r_append_prefix.restype = st
+    L.a8r_export_prefix.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    _c_void_p, _c_void_p]
+    L.a8r_export_prefix.restype = st
+    L.a8r_clear_prefix.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32]
+    L.a8r_clear_prefix.restype = st
+    L.a8r_prefix_length.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, _i32p]
+    L.a8r_prefix_length.restype = st
     L.a8r_get_state.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, _i64p, _i32p, _i32p]
     L.a8r_get_state.restype = st
     L.a8r_read_ring.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, _c_void_p, _c_void_p]
@@ -149,12 +160,12 @@ def _i32_array(vals):
 
 def make_config(n_layers, n_streams, n_q_heads, n_kv_heads, head_dim, window, max_chunk=1,
                 bf16=True, rope_theta=1.0e6, softmax_scale=0.0, portable=False,
-                rebase_on_evict=False) -> Config:
+                rebase_on_evict=False, prefix_capacity=0) -> Config:
     return Config(n_layers, n_streams, n_q_heads, n_kv_heads, head_dim, window, max_chunk,
                   A8R_BF16 if bf16 else A8R_F32,
                   A8R_KERNELS_PORTABLE if portable else A8R_KERNELS_AUTO,
                   A8R_REBASE_ON_EVICT if rebase_on_evict else A8R_ROTATE_ON_READ,
-                  float(rope_theta), float(softmax_scale), 0.0)
+                  float(rope_theta), float(softmax_scale), 0.0, int(prefix_capacity), 0)
 
 
 def workspace_bytes(cfg: Config) -> int:
@@ -272,6 +283,20 @@ class Cache:
 
     def get_state(self, layer, b):
         return get_state(self.handle, layer, b)
+
+    def append_prefix(self, layer, b0, nb, n_new, k, v):
+        _check(lib().a8r_append_prefix(self.handle, layer, b0, nb, n_new, _ptr(k), _ptr(v)))
+
+    def export_prefix(self, layer, b0, nb, n, k_out, v_out):
+        _check(lib().a8r_export_prefix(self.handle, layer, b0, nb, n, _ptr(k_out), _ptr(v_out)))
+
+    def clear_prefix(self, b0, nb):
+        _check(lib().a8r_clear_prefix(self.handle, b0, nb))
+
+    def prefix_length(self, layer, b):
+        f = ctypes.c_int32()
+        _check(lib().a8r_prefix_length(self.handle, layer, b, ctypes.byref(f)))
+        return f.value
 
     def read_ring(self, layer, b):
         c = self.cfg

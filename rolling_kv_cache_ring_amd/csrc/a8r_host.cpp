@@ -115,8 +115,9 @@ struct Ledger {
 };
 
 struct Layout {
-    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, counter_off, part_t_off, part_x_off, total;
-    int w_pad, rows_max;
+    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, counter_off, part_t_off,
+        part_x_off, total;
+    int w_pad, f_pad, rows_max;
 };
 
 bool mul_ok(size_t a, size_t b, size_t* out) {
@@ -141,7 +142,11 @@ a8r_status validate_config(const a8r_config* c) {
         return fail(A8R_EINVAL, "kernel_policy %d", c->kernel_policy);
     if (c->cache_mode != A8R_ROTATE_ON_READ && c->cache_mode != A8R_REBASE_ON_EVICT)
         return fail(A8R_EINVAL, "cache_mode %d", c->cache_mode);
-    if (c->reserved_f != 0.f) return fail(A8R_EINVAL, "reserved_f must be 0");
+    if (c->reserved_f != 0.f || c->reserved != 0) return fail(A8R_EINVAL, "reserved fields must be 0");
+    if (c->prefix_capacity < 0 || c->prefix_capacity > (1 << 20))
+        return fail(A8R_EINVAL, "prefix_capacity %d out of [0, 2^20]", c->prefix_capacity);
+    if (c->prefix_capacity > 0 && c->cache_mode == A8R_REBASE_ON_EVICT)
+        return fail(A8R_EUNSUPPORTED, "a pinned prefix is not available with A8R_REBASE_ON_EVICT");
     if (!(c->rope_theta > 0.0) || !isfinite(c->rope_theta)) return fail(A8R_EINVAL, "rope_theta must be > 0");
     if (!isfinite(c->softmax_scale)) return fail(A8R_EINVAL, "softmax_scale must be finite");
     if ((int64_t)c->n_q_heads * (int64_t)c->n_streams > (1 << 24))
@@ -155,11 +160,13 @@ a8r_status compute_layout(const a8r_config* c, Layout* lay) {
     const int group = c->n_q_heads / c->n_kv_heads;
     const int qmax = c->max_chunk < a8r::kMaxPartialQ ? c->max_chunk : a8r::kMaxPartialQ;
     const int rows_max = qmax * group;
+    const int f_pad = (int)((c->prefix_capacity + a8r::kTile - 1) / a8r::kTile * a8r::kTile);
     size_t pairs, ring, t;
     if (!mul_ok((size_t)c->n_layers * c->n_streams, (size_t)c->n_kv_heads, &pairs) ||
-        !mul_ok(pairs, (size_t)w_pad * c->head_dim, &t) || !mul_ok(t, eb, &ring))
+        !mul_ok(pairs, (size_t)(w_pad + f_pad) * c->head_dim, &t) || !mul_ok(t, eb, &ring))
         return fail(A8R_EINVAL, "ring size overflows size_t");
-    const size_t table = (size_t)(c->window + a8r::kTablePad) * (c->head_dim / 2) * 8;
+    // rows up to W + f_pad: a query at most W - 1 + F indices past a prefix tile
+    const size_t table = (size_t)(c->window + f_pad + a8r::kTablePad) * (c->head_dim / 2) * 8;
     const size_t state = (size_t)c->n_layers * c->n_streams * sizeof(a8r::DevState);
     const size_t prow = (size_t)c->n_streams * c->n_kv_heads * a8r::kMaxSplits * rows_max;
     size_t off = 0;
@@ -188,6 +195,7 @@ a8r_status compute_layout(const a8r_config* c, Layout* lay) {
                         a8r::kAlign);
     lay->total = off;
     lay->w_pad = w_pad;
+    lay->f_pad = f_pad;
     lay->rows_max = rows_max;
     return A8R_OK;
 }
@@ -198,9 +206,9 @@ a8r_status compute_layout(const a8r_config* c, Layout* lay) {
 // theta per "Audio8-ASR-0.1B in audio.cpp", section "Architecture".  Row r is
 // the rotation for re-based index r; indices are always small (< W + 32), so
 // the float64 angle is exact to ~1e-16 relative.
-std::vector<float> build_table(int window, int head_dim, double theta) {
+std::vector<float> build_table(int window, int f_pad, int head_dim, double theta) {
     const int np = head_dim / 2;
-    const int rows = window + a8r::kTablePad;
+    const int rows = window + f_pad + a8r::kTablePad;
     std::vector<double> inv(np);
     for (int i = 0; i < np; ++i) inv[i] = pow(theta, -2.0 * i / head_dim);
     std::vector<float> t((size_t)rows * np * 2);
@@ -224,6 +232,7 @@ struct a8r_cache {
     hipStream_t stream = nullptr;
     void* base = nullptr;
     mutable uint32_t epoch = 0;   // launch counter; tags decode split partials (never 0)
+    std::vector<int32_t> prefix;  // pinned prefix length per (layer, stream)
     bool owns = false;
     bool poisoned = false;
     int device = 0;
@@ -290,6 +299,7 @@ a8r_status a8r_cache_create(const a8r_config* cfg, void* hip_stream, void* works
     c->lay = lay;
     c->stream = (hipStream_t)hip_stream;
     c->ledger.init(cfg->n_layers, cfg->n_streams, cfg->window);
+    c->prefix.assign((size_t)cfg->n_layers * cfg->n_streams, 0);
 
     hipError_t e = hipGetDevice(&c->device);
     if (e != hipSuccess) {
@@ -328,13 +338,15 @@ a8r_status a8r_cache_create(const a8r_config* cfg, void* hip_stream, void* works
     g.d = cfg->head_dim;
     g.window = cfg->window;
     g.w_pad = lay.w_pad;
+    g.f_pad = lay.f_pad;
+    g.pair_slots = lay.w_pad + lay.f_pad;
     g.elem_bytes = cfg->dtype == A8R_BF16 ? 2 : 4;
     g.prerot = cfg->cache_mode == A8R_REBASE_ON_EVICT;
     g.rows_max = lay.rows_max;
     const double scale = cfg->softmax_scale > 0.f ? (double)cfg->softmax_scale : 1.0 / sqrt((double)cfg->head_dim);
     g.scale_log2 = (float)(scale * 1.4426950408889634);  // log2(e)
 
-    const std::vector<float> table = build_table(cfg->window, cfg->head_dim, cfg->rope_theta);
+    const std::vector<float> table = build_table(cfg->window, lay.f_pad, cfg->head_dim, cfg->rope_theta);
     e = hipMemsetAsync(c->base, 0, lay.total, c->stream);
     if (e == hipSuccess)   // every exchange slot starts empty (all ones)
         e = hipMemsetAsync(b + lay.part_x_off, 0xff, lay.total - lay.part_x_off, c->stream);
@@ -380,6 +392,7 @@ void fill_batch(const a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, a8r::
         const PairState& p = c->ledger.at(layer, b0 + i);
         sb->next_slot[i] = p.next_slot;
         sb->length[i] = p.length;
+        sb->prefix[i] = c->prefix[(size_t)layer * c->cfg.n_streams + b0 + i];
         sb->next_pos[i] = p.next_pos;
     }
 }
@@ -493,6 +506,76 @@ a8r_status a8r_append_decode_attn(a8r_cache* c, int32_t layer, int32_t b0, int32
     return ok();
 }
 
+a8r_status a8r_append_prefix(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_new, const void* k,
+                             const void* v) {
+    a8r_status st = check_live(c);
+    if (st != A8R_OK) return st;
+    if ((st = check_streams(c, layer, b0, nb)) != A8R_OK) return st;
+    if (c->cfg.prefix_capacity == 0) return fail(A8R_EUNSUPPORTED, "the cache has no prefix capacity");
+    if (n_new < 1) return fail(A8R_EINVAL, "n_new %d < 1", n_new);
+    if (!k || !v) return fail(A8R_EINVAL, "k or v is NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(A8R_EINVAL, "k and v must be 16-byte aligned");
+    for (int32_t i = 0; i < nb; ++i) {
+        const size_t at = (size_t)layer * c->cfg.n_streams + b0 + i;
+        if (c->ledger.at(layer, b0 + i).length != 0)
+            return fail(A8R_ESTATE, "stream %d layer %d: the prefix must precede the window (L = %d)", b0 + i,
+                        layer, c->ledger.at(layer, b0 + i).length);
+        if (c->prefix[at] + n_new > c->cfg.prefix_capacity)
+            return fail(A8R_EINVAL, "stream %d layer %d: prefix %d + %d exceeds capacity %d", b0 + i, layer,
+                        c->prefix[at], n_new, c->cfg.prefix_capacity);
+    }
+    const size_t row = (size_t)n_new * c->cfg.n_kv_heads * c->cfg.head_dim * c->geo.elem_bytes;
+    for (int32_t i0 = 0; i0 < nb; i0 += a8r::kBatch) {
+        a8r::StreamBatch sb;
+        fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
+        hipError_t e = a8r::launch_append_prefix(c->geo, layer, sb, n_new, (const uint8_t*)k + i0 * row,
+                                                 (const uint8_t*)v + i0 * row, c->stream);
+        if (e != hipSuccess) return device_fail(c, e, "prefix append kernel");
+    }
+    for (int32_t i = 0; i < nb; ++i) c->prefix[(size_t)layer * c->cfg.n_streams + b0 + i] += n_new;
+    return ok();
+}
+
+a8r_status a8r_export_prefix(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n, void* k, void* v) {
+    a8r_status st = check_live(c);
+    if (st != A8R_OK) return st;
+    if ((st = check_streams(c, layer, b0, nb)) != A8R_OK) return st;
+    if (n < 1) return fail(A8R_EINVAL, "n %d < 1", n);
+    if (!k || !v) return fail(A8R_EINVAL, "k or v is NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(A8R_EINVAL, "k and v must be 16-byte aligned");
+    for (int32_t i = 0; i < nb; ++i) {
+        const int32_t f = c->prefix[(size_t)layer * c->cfg.n_streams + b0 + i];
+        if (f != n) return fail(A8R_EINVAL, "stream %d layer %d: prefix length %d, not %d", b0 + i, layer, f, n);
+    }
+    const size_t row = (size_t)n * c->cfg.n_kv_heads * c->cfg.head_dim * c->geo.elem_bytes;
+    for (int32_t i0 = 0; i0 < nb; i0 += a8r::kBatch) {
+        a8r::StreamBatch sb;
+        fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
+        hipError_t e = a8r::launch_export_prefix(c->geo, layer, sb, n, (uint8_t*)k + i0 * row,
+                                                 (uint8_t*)v + i0 * row, c->stream);
+        if (e != hipSuccess) return device_fail(c, e, "prefix export kernel");
+    }
+    return ok();
+}
+
+a8r_status a8r_clear_prefix(a8r_cache* c, int32_t b0, int32_t nb) {
+    a8r_status st = check_live(c);
+    if (st != A8R_OK) return st;
+    if ((st = check_streams(c, 0, b0, nb)) != A8R_OK) return st;
+    for (int32_t layer = 0; layer < c->cfg.n_layers; ++layer)
+        for (int32_t i = 0; i < nb; ++i) c->prefix[(size_t)layer * c->cfg.n_streams + b0 + i] = 0;
+    return ok();
+}
+
+a8r_status a8r_prefix_length(a8r_cache* c, int32_t layer, int32_t b, int32_t* length) {
+    a8r_status st = check_live(c);
+    if (st != A8R_OK) return st;
+    if ((st = check_streams(c, layer, b, 1)) != A8R_OK) return st;
+    if (!length) return fail(A8R_EINVAL, "length is NULL");
+    *length = c->prefix[(size_t)layer * c->cfg.n_streams + b];
+    return ok();
+}
+
 a8r_status a8r_get_state(a8r_cache* c, int32_t layer, int32_t b, int64_t* next_pos, int32_t* length,
                          int32_t* next_slot) {
     a8r_status st = check_live(c);
@@ -520,7 +603,7 @@ a8r_status a8r_read_ring(a8r_cache* c, int32_t layer, int32_t b, void* k_host, v
     if (st != A8R_OK) return st;
     if ((st = check_streams(c, layer, b, 1)) != A8R_OK) return st;
     const a8r::Geometry& g = c->geo;
-    const size_t eb = g.elem_bytes, D = g.d, W = g.window, wp = g.w_pad, H = g.hkv;
+    const size_t eb = g.elem_bytes, D = g.d, W = g.window, wp = g.pair_slots, H = g.hkv;
     const size_t per_head = wp * D * eb;
     std::vector<uint8_t> tmp(per_head * H);
     hipError_t e = hipStreamSynchronize(c->stream);

@@ -48,13 +48,14 @@ struct StreamBatch {
     uint32_t epoch;     // nonzero, different for every launch of a cache (tags split partials)
     int32_t next_slot[kBatch];
     int32_t length[kBatch];
+    int32_t prefix[kBatch];   // pinned prefix length F (re-based indices 0 .. F-1; the window follows)
     int64_t next_pos[kBatch];
 };
 
 // Everything a kernel needs to find a (layer, stream, kv head) window.
 struct Geometry {
-    void* k_ring;
-    void* v_ring;
+    void* k_ring;       // [layer][stream][kv_head][pair_slots][D]: ring slots 0 .. W-1, then the
+    void* v_ring;       // pinned prefix at slots w_pad .. w_pad + F - 1 (V: 8-slot blocks transposed)
     const float2* table;
     DevState* state;
     float* part_o;      // split partials: [n_streams][n_kv_heads][kMaxSplits][rows_max][D]
@@ -65,6 +66,8 @@ struct Geometry {
     uint64_t* part_x;   // two-split decode exchange slots, one per output element:
                         // [n_streams][n_kv_heads][kMaxGroupTagged][D], kSlotEmpty between calls
     int n_layers, n_streams, hq, hkv, group, d, window, w_pad;
+    int f_pad;          // prefix capacity rounded up to 32 (0: no prefix)
+    int pair_slots;     // w_pad + f_pad: slots per (layer, stream, kv head)
     int elem_bytes;     // 2 (bf16) or 4 (f32)
     int prerot;         // keys are stored rotated to their re-based index (A8R_REBASE_ON_EVICT)
     int rows_max;       // max(1, min(max_chunk, kMaxPartialQ)) * group
@@ -85,6 +88,12 @@ hipError_t launch_reset(const Geometry& g, const StreamBatch& after, hipStream_t
 // append): rotates the new tokens' keys to their re-based indices and, where
 // the append evicted e tokens, every surviving key by R(-e), in place.
 hipError_t launch_rebase(const Geometry& g, int layer, const StreamBatch& before, int n, hipStream_t s);
+// Writes n tokens into the pinned prefix of a batch at prefix slots F .. F+n-1.
+hipError_t launch_append_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, const void* k,
+                                const void* v, hipStream_t s);
+// Copies the n prefix tokens of each stream out to k, v [nb][n][Hkv][D].
+hipError_t launch_export_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, void* k, void* v,
+                                hipStream_t s);
 // Copies n_new tokens per stream into the ring; `before` is the state before.
 hipError_t launch_append(const Geometry& g, int layer, const StreamBatch& before, int n_new,
                          const void* k, const void* v, hipStream_t s);

@@ -24,6 +24,13 @@
 //                      in groups of up to 128 per block): keys rotated once
 //                      per visit into an LDS tile, QK^T and PV on MFMA,
 //                      software-pipelined
+//   prefix_append_kernel, prefix_export_kernel
+//                      a pinned prompt prefix (never evicted, attended before
+//                      the window) into and out of its slots after the ring
+//   rebase_kernel      the rebase-on-evict comparison variant's re-rotation
+//
+// The attention kernels take the prefix as extra tiles after the ring's; the
+// prefix walk is a template flag, instantiated only for batches that hold one.
 //
 // Every kernel takes the ring state of its streams from its launch arguments
 // (StreamBatch, filled by the host from its bookkeeping when the call is made).
@@ -99,13 +106,12 @@ __global__ void reset_kernel(Geometry g, StreamBatch r) {
 // K rows are row-major; element d of V for slot s lives at ((s/8)*D + d)*8 + s%8
 // of the head's V block array.
 template <int EB>
-__device__ __forceinline__ void write_token_vals(const Geometry& g, int64_t pair, int slot, int c, u32x4 kv,
-                                                 u32x4 vv) {
+__device__ __forceinline__ void store_token(void* k_base, void* v_base, int pad, int D, int64_t pair, int slot,
+                                            int c, u32x4 kv, u32x4 vv) {
     constexpr int per16 = 16 / EB;
-    const int D = g.d;
-    uint8_t* kdst = (uint8_t*)g.k_ring + ((pair * g.w_pad + slot) * D + (int64_t)c * per16) * EB;
+    uint8_t* kdst = (uint8_t*)k_base + ((pair * pad + slot) * D + (int64_t)c * per16) * EB;
     *(u32x4*)kdst = kv;
-    uint8_t* vblk = (uint8_t*)g.v_ring + ((pair * (g.w_pad / 8) + slot / 8) * (int64_t)D * 8) * EB;
+    uint8_t* vblk = (uint8_t*)v_base + ((pair * (pad / 8) + slot / 8) * (int64_t)D * 8) * EB;
     const int lane8 = slot & 7;
 #pragma unroll
     for (int u = 0; u < per16; ++u) {
@@ -117,6 +123,12 @@ __device__ __forceinline__ void write_token_vals(const Geometry& g, int64_t pair
             ((uint32_t*)vblk)[(int64_t)d * 8 + lane8] = vv[u];
         }
     }
+}
+
+template <int EB>
+__device__ __forceinline__ void write_token_vals(const Geometry& g, int64_t pair, int slot, int c, u32x4 kv,
+                                                 u32x4 vv) {
+    store_token<EB>(g.k_ring, g.v_ring, g.pair_slots, g.d, pair, slot, c, kv, vv);
 }
 
 template <int EB>
@@ -152,6 +164,67 @@ __global__ __launch_bounds__(256) void append_kernel(Geometry g, int layer, Stre
     }
 }
 
+// Pinned prefix: token j of stream b goes to prefix slot F + j (pair slot
+// w_pad + F + j, after the ring; never evicted).
+template <int EB>
+__global__ __launch_bounds__(256) void prefix_append_kernel(Geometry g, int layer, StreamBatch st, int n_new,
+                                                            const uint8_t* __restrict__ k,
+                                                            const uint8_t* __restrict__ v) {
+    const int bi = blockIdx.x, b = st.b0 + bi;
+    const int D = g.d;
+    constexpr int per16 = 16 / EB;
+    const int chunks = D / per16;
+    const int total = n_new * g.hkv * chunks;
+    const int f0 = st.prefix[bi];
+    for (int t = threadIdx.x; t < total; t += blockDim.x) {
+        const int c = t % chunks;
+        const int rest = t / chunks;
+        const int kh = rest % g.hkv, j = rest / g.hkv;
+        const int64_t src = ((((int64_t)bi * n_new + j) * g.hkv + kh) * D + (int64_t)c * per16) * EB;
+        store_token<EB>(g.k_ring, g.v_ring, g.pair_slots, D, pair_index(g, layer, b, kh), g.w_pad + f0 + j, c,
+                        *(const u32x4*)(k + src), *(const u32x4*)(v + src));
+    }
+}
+
+// Export of a pinned prefix: prefix token j of stream b back to row j of the
+// append layout [nb][n][Hkv][D] (the inverse of prefix_append_kernel: K rows as
+// stored, V gathered back out of its transposed 8-slot blocks).
+template <int EB>
+__global__ __launch_bounds__(256) void prefix_export_kernel(Geometry g, int layer, StreamBatch st, int n,
+                                                            uint8_t* __restrict__ k, uint8_t* __restrict__ v) {
+    const int bi = blockIdx.x, b = st.b0 + bi;
+    const int D = g.d;
+    constexpr int per16 = 16 / EB;
+    const int chunks = D / per16;
+    const int total = n * g.hkv * chunks;
+    for (int t = threadIdx.x; t < total; t += blockDim.x) {
+        const int c = t % chunks;
+        const int rest = t / chunks;
+        const int kh = rest % g.hkv, j = rest / g.hkv;
+        const int64_t dst = ((((int64_t)bi * n + j) * g.hkv + kh) * D + (int64_t)c * per16) * EB;
+        const int64_t pair = pair_index(g, layer, b, kh);
+        const int slot = g.w_pad + j;
+        *(u32x4*)(k + dst) =
+            *(const u32x4*)((const uint8_t*)g.k_ring + ((pair * g.pair_slots + slot) * D + (int64_t)c * per16) * EB);
+        const uint8_t* vblk =
+            (const uint8_t*)g.v_ring + ((pair * (g.pair_slots / 8) + slot / 8) * (int64_t)D * 8) * EB;
+        const int lane8 = slot & 7;
+        u32x4 vv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if constexpr (EB == 2) {
+                const int d = c * per16 + 2 * u;
+                const uint32_t lo = ((const uint16_t*)vblk)[(int64_t)d * 8 + lane8];
+                const uint32_t hi = ((const uint16_t*)vblk)[(int64_t)(d + 1) * 8 + lane8];
+                vv[u] = lo | (hi << 16);
+            } else {
+                vv[u] = ((const uint32_t*)vblk)[(int64_t)(c * per16 + u) * 8 + lane8];
+            }
+        }
+        *(u32x4*)(v + dst) = vv;
+    }
+}
+
 // ------------------------------------------------------ rebase on evict ----
 // A8R_REBASE_ON_EVICT (a comparison variant): keys are stored rotated to their
 // re-based index.  After an append of n tokens to a window of L0 keys (state
@@ -175,7 +248,7 @@ __global__ __launch_bounds__(256) void rebase_kernel(Geometry g, int layer, Stre
     const int r_begin = e > 0 ? r0 : max(r0, r_new);   // without an eviction only new keys change
     const int r_end = min(r0 + 256, L1);
     if (r_begin >= r_end) return;
-    uint8_t* kring = (uint8_t*)g.k_ring + pair_index(g, layer, b, kh) * g.w_pad * D * EB;
+    uint8_t* kring = (uint8_t*)g.k_ring + pair_index(g, layer, b, kh) * g.pair_slots * D * EB;
     const int cnt = (r_end - r_begin) * NP;
     for (int t = threadIdx.x; t < cnt; t += 256) {
 #pragma clang fp contract(off)
@@ -278,8 +351,11 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
     int oldest = st.next_slot[bi] - L;
     if (oldest < 0) oldest += W;
     const int64_t pair = pair_index(g, layer, b, kh);
-    const void* kring = (const uint8_t*)g.k_ring + pair * g.w_pad * D * EB;
-    const void* vring = (const uint8_t*)g.v_ring + pair * g.w_pad * D * EB;
+    const void* kring = (const uint8_t*)g.k_ring + pair * g.pair_slots * D * EB;
+    const void* vring = (const uint8_t*)g.v_ring + pair * g.pair_slots * D * EB;
+    // the pinned prefix (F tokens, pair slots w_pad ..) precedes the window: key
+    // index r in [-F, L)
+    const int F = st.prefix[bi];
 
     // rotated, scaled queries: query c has re-based index L - n_q + c
     for (int idx = tid; idx < RG * NP; idx += 256) {
@@ -308,15 +384,25 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 #pragma unroll
     for (int i = 0; i < DQ; ++i) o[i] = 0.f;
 
-    const int n_kt = (L + KT - 1) / KT;
+    const int n_kt = (F + L + KT - 1) / KT;
     const int per = (n_kt + n_split - 1) / n_split;
     const int kt0 = split * per, kt1 = min(n_kt, kt0 + per);
     for (int kt = kt0; kt < kt1; ++kt) {
         __syncthreads();
         for (int idx = tid; idx < KT * NP; idx += 256) {
-            const int j = idx / NP, i = idx - j * NP, r = kt * KT + j;
+            const int j = idx / NP, i = idx - j * NP, r = kt * KT + j - F;
             float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
-            if (r < L) {
+            if (r < 0) {                       // prefix token r + F at index r: R(r) = R(-r) conjugated
+                const int jp = g.w_pad + r + F;
+                const float x1 = load_elem<EB>(kring, (int64_t)jp * D + i);
+                const float x2 = load_elem<EB>(kring, (int64_t)jp * D + i + NP);
+                const float2 cs = g.table[(int64_t)(-r) * NP + i];
+                k1 = x1 * cs.x + x2 * cs.y;
+                k2 = x2 * cs.x - x1 * cs.y;
+                const int64_t vb = (int64_t)(jp >> 3) * D * 8 + (jp & 7);
+                v1 = load_elem<EB>(vring, vb + (int64_t)i * 8);
+                v2 = load_elem<EB>(vring, vb + (int64_t)(i + NP) * 8);
+            } else if (r < L) {
                 const int slot = wrap_slot(oldest + r, W);
                 const float x1 = load_elem<EB>(kring, (int64_t)slot * D + i);
                 const float x2 = load_elem<EB>(kring, (int64_t)slot * D + i + NP);
@@ -338,7 +424,7 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
         float mx = -INFINITY;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int j = sub * 4 + jj, r = kt * KT + j;
+            const int j = sub * 4 + jj, r = kt * KT + j - F;
             float acc = 0.f;
             for (int d = 0; d < D; ++d) acc += qs[my_row][d] * ks[j][d];
             s[jj] = (row_ok && r < L && r <= my_rq) ? acc : -INFINITY;
@@ -438,6 +524,9 @@ struct DecodeCtx {
     const uint16_t* vp;
     const float2* table;
     int oldest, t_o, p0t, n_tiles, L, W, rq, tb0, tb1, gq, n;
+    int n_roll, F;     // visits over the ring, then ceil(F / 32) over the prefix
+    int pre_on;        // a pinned prefix may exist (compile-time in every kernel: without it
+                       // the visit walk has no prefix branch)
     int prerot;        // keys stored rotated to their index: only the query is rotated
     float scale_log2;
 };
@@ -451,6 +540,32 @@ __device__ __forceinline__ int visit_rho(const DecodeCtx& c, int k, int s0) {
     if (k == 0) return -c.t_o;
     const int rho = s0 - c.oldest;
     return rho < 0 ? rho + c.W : rho;
+}
+
+// Where visit k reads from: the ring's tiles first (k < n_roll), then the pinned
+// prefix's tiles, stored after the ring (tile n_tiles + m holds prefix tokens
+// 32m .. 32m + 31, those below F live).  Relative to the window's origin a
+// prefix token's re-based index is 32m + t - F < 0: the prefix sits just
+// before the window (indices taken over [prefix; window]).  s0 is the tile's
+// first slot, or for a prefix tile its first prefix token.
+struct VisitSrc {
+    int tile, s0, rho;
+    bool pre;
+};
+
+__device__ __forceinline__ VisitSrc visit_src(const DecodeCtx& c, int k) {
+    VisitSrc v;
+    v.pre = c.pre_on && k >= c.n_roll;
+    if (!v.pre) {
+        v.tile = visit_tile(c, k);
+        v.s0 = v.tile * kTile;
+        v.rho = visit_rho(c, k, v.s0);
+    } else {
+        v.s0 = (k - c.n_roll) * kTile;
+        v.tile = c.n_tiles + k - c.n_roll;
+        v.rho = v.s0 - c.F;
+    }
+    return v;
 }
 
 // (cos, sin) of the lane's 8*(D/64) pairs (dims 8*gq + 32*kk + e, kk < D/64)
@@ -558,24 +673,23 @@ __device__ __forceinline__ void dma_table_row(const float2* table, int row, int 
 template <int D, bool CHUNK = false>
 __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, unsigned char* kbuf) {
     constexpr int RPI = 64 / (D / 8);            // rows per instruction
-    const int p = visit_tile(c, k);
-    const int s0 = p * kTile;
+    const VisitSrc vs = visit_src(c, k);
     const int rl = lane / (D / 8), sl = lane % (D / 8);
 #pragma unroll
     for (int j = 0; j < 2 * (D / 32); ++j) {
         const int r = RPI * j + rl;
         const int col = 8 * (sl >> 3) + ((sl & 7) ^ k_swz(r));
-        dma16(c.kp + (int64_t)(s0 + r) * D + 8 * col, kbuf + j * 1024);
+        dma16(c.kp + (int64_t)(vs.tile * kTile + r) * D + 8 * col, kbuf + j * 1024);
     }
-    const int rho = visit_rho(c, k, s0);
+    const int rho = vs.rho;
     dma_table_row<D>(c.table, CHUNK ? (rho < 0 ? -rho : rho) : c.rq - (c.prerot ? 0 : rho), lane,
                      kbuf + 2 * (D / 32) * 1024);
 }
 
 template <int D>
 __device__ __forceinline__ void dec_load_v(const DecodeCtx& c, int k, unsigned char* vbuf) {
-    const int p = visit_tile(c, k);
-    const uint16_t* vb = c.vp + ((int64_t)(p * 4 + c.gq) * D + c.n) * 8;
+    const VisitSrc vs = visit_src(c, k);
+    const uint16_t* vb = c.vp + ((int64_t)(vs.tile * 4 + c.gq) * D + c.n) * 8;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) dma16(vb + (int64_t)nb * 16 * 8, vbuf + nb * 1024);
 }
@@ -625,9 +739,8 @@ __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const De
                                              const float4 (&cf1)[D / 64][4], floatx4 (&o)[D / 16], float& m,
                                              float& l) {
     constexpr int KK = D / 32, NB = D / 16;
-    const int p = visit_tile(c, k);
-    const int s0 = p * kTile;
-    const int rho = visit_rho(c, k, s0);
+    const VisitSrc vs = visit_src(c, k);
+    const int s0 = vs.s0, rho = vs.rho;
     bf16x8 qb[KK];
     rotate_row<D>(r.qc, qraw, qb);            // query by R(r_q - rho)
     const bool seam = (k == 0) && (c.t_o > 0);
@@ -644,14 +757,17 @@ __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const De
     const float sl = c.scale_log2;
     float s[8] = {sc0[0] * sl, sc0[1] * sl, sc0[2] * sl, sc0[3] * sl,
                   sc1[0] * sl, sc1[1] * sl, sc1[2] * sl, sc1[3] * sl};
-    const bool full = (k != 0) && (rho + kTile <= c.L) && (s0 + kTile <= c.W);
+    const bool full = vs.pre ? (s0 + kTile <= c.F) : ((k != 0) && (rho + kTile <= c.L) && (s0 + kTile <= c.W));
     if (!full) {
-        // branch-free: key index of each score, then a select
+        // branch-free: key index of each score, then a select (a prefix tile:
+        // its live tokens, all before the query)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int tt = 8 * c.gq + e;
             const int rr = rho + tt + ((seam & (tt < c.t_o)) ? c.W : 0);
-            const bool ok = (rr >= 0) & (rr < c.L) & (s0 + tt < c.W);
+            const bool ok_ring = (rr >= 0) & (rr < c.L) & (s0 + tt < c.W);
+            const bool ok_pre = s0 + tt < c.F;
+            const bool ok = vs.pre ? ok_pre : ok_ring;
             s[e] = ok ? s[e] : -INFINITY;
         }
     }
@@ -717,7 +833,7 @@ __device__ __forceinline__ void patch_v(unsigned char* vbuf, int t, int lane, u3
     }
 }
 
-template <int D>
+template <int D, bool PREROT, bool PRE>
 __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, StreamBatch st,
                                                       const uint16_t* __restrict__ q,
                                                       uint16_t* __restrict__ out, int n_split,
@@ -768,11 +884,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     c.gq = gq;
     c.n = n;
     c.scale_log2 = g.scale_log2;
-    c.prerot = g.prerot;
+    c.prerot = PREROT;   // compile-time constants: the method's instance carries none of the variant
+    c.pre_on = PRE;      // and, without a prefix in the batch, none of the prefix walk
     c.table = g.table;
     const int64_t pair = pair_index(g, layer, b, kh);
-    c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
-    c.vp = (const uint16_t*)g.v_ring + pair * g.w_pad * D;
+    c.kp = (const uint16_t*)g.k_ring + pair * g.pair_slots * D;
+    c.vp = (const uint16_t*)g.v_ring + pair * g.pair_slots * D;
     int n_visit;
     {
         int last = c.oldest + L - 1;
@@ -784,6 +901,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             if (n_visit > c.n_tiles) n_visit = c.n_tiles;
         }
     }
+    // then the pinned prefix's tiles
+    c.F = PRE ? st.prefix[bi] : 0;
+    c.n_roll = n_visit;
+    n_visit += (c.F + kTile - 1) / kTile;
     const int per = (n_visit + n_split - 1) / n_split;
     const int k0 = split * per, k1 = min(n_visit, k0 + per);
 
@@ -1177,7 +1298,7 @@ struct PipeBuf {
     static constexpr int nV = (D / 16) / 4;
 };
 
-template <int D, int NW, int WG>
+template <int D, int NW, int WG, bool PRE>
 __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer, StreamBatch st, int C,
                                                      const uint16_t* __restrict__ q,
                                                      uint16_t* __restrict__ out, int n_split) {
@@ -1217,10 +1338,11 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     c.n = n;
     c.scale_log2 = g.scale_log2;
     c.prerot = 0;
+    c.pre_on = PRE;
     c.table = g.table;
     const int64_t pair = pair_index(g, layer, b, kh);
-    c.kp = (const uint16_t*)g.k_ring + pair * g.w_pad * D;
-    c.vp = (const uint16_t*)g.v_ring + pair * g.w_pad * D;
+    c.kp = (const uint16_t*)g.k_ring + pair * g.pair_slots * D;
+    c.vp = (const uint16_t*)g.v_ring + pair * g.pair_slots * D;
     int n_visit;
     {
         int last = c.oldest + L - 1;
@@ -1232,6 +1354,10 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
             if (n_visit > c.n_tiles) n_visit = c.n_tiles;
         }
     }
+    // then the pinned prefix's tiles
+    c.F = PRE ? st.prefix[bi] : 0;
+    c.n_roll = n_visit;
+    n_visit += (c.F + kTile - 1) / kTile;
     const int per = (n_visit + n_split - 1) / n_split;
     const int k0 = split * per, k1 = min(n_visit, k0 + per);
     // group wg takes visits k0 + wg, k0 + wg + WG, ...: its local visit v is
@@ -1246,22 +1372,21 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     // is always in range; its slot is never read)
     auto issue_k = [&](int v, unsigned char* slot) {
         const int kv = v < n_mine ? kvis(v) : 0;
-        const int p = visit_tile(c, kv);
-        const int s0 = p * kTile;
-        const unsigned char* krow = (const unsigned char*)(c.kp + (int64_t)s0 * D);
+        const VisitSrc vs = visit_src(c, kv);
+        const unsigned char* krow = (const unsigned char*)(c.kp + (int64_t)vs.tile * kTile * D);
 #pragma unroll
         for (int u = 0; u < PB::nK - 1; ++u) {
             const int j = wave * (PB::nK - 1) + u;
             dma16(krow + j * 1024 + 16 * lane, slot + j * 1024);
         }
-        const int rho = visit_rho(c, kv, s0);
+        const int rho = vs.rho;
         const unsigned char* row = (const unsigned char*)(c.table + (int64_t)(rho < 0 ? -rho : rho) * (D / 2));
         constexpr int q4 = PB::kC / 4;                  // bytes of the row per wave
         if (lane < q4 / 16) dma16(row + wave * q4 + 16 * lane, slot + PB::kK + wave * q4);
     };
     auto issue_v = [&](int v, unsigned char* slot) {
-        const int p = visit_tile(c, v < n_mine ? kvis(v) : 0);
-        const uint16_t* vb = c.vp + ((int64_t)(p * 4 + gq) * D + n) * 8;
+        const VisitSrc vs = visit_src(c, v < n_mine ? kvis(v) : 0);
+        const uint16_t* vb = c.vp + ((int64_t)(vs.tile * 4 + gq) * D + n) * 8;
 #pragma unroll
         for (int u = 0; u < PB::nV; ++u) {
             const int nb = wave * PB::nV + u;
@@ -1418,8 +1543,10 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         if (n_mine > 2) issue_k(2, ring_k + 2 * PB::kKC);
         if (n_mine > 1) issue_v(1, ring_v + PB::kV);
         if (n_mine > 0) {
+            // the first visit of the ring (rho = -t_o) and prefix visits (rho < 0)
+            // compose R(rho) from the conjugate of row |rho|
             const int kv = kvis(0);
-            rotate(ring_k, tiles, kv == 0, kv == 0 && c.t_o > 0);
+            rotate(ring_k, tiles, kv == 0 || (PRE && kv >= c.n_roll), kv == 0 && c.t_o > 0);
         }
         __builtin_amdgcn_s_waitcnt(kLgkm0);
     }
@@ -1472,9 +1599,8 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         if (s + 2 < n_mine) issue_v(s + 2, ring_v + ((S + 2) % 3) * PB::kV);
 
         const int kv = kvis(s);
-        const int p = visit_tile(c, kv);
-        const int s0 = p * kTile;
-        const int rho = visit_rho(c, kv, s0);
+        const VisitSrc vs = visit_src(c, kv);
+        const int s0 = vs.s0, rho = vs.rho;
         const bool seam = (kv == 0) && (c.t_o > 0);
         const bool cmp = do_c && act0;                 // a wave without query rows only rotates
         // QK^T of visit s first, so that the rotation's VALU work below runs
@@ -1505,9 +1631,11 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
                 }
             }
         }
-        if (do_r) rotate(ring_k + ((S + 1) % 3) * PB::kKC, tiles + ((S + 1) % 2) * PB::kT, false, false);
+        if (do_r)
+            rotate(ring_k + ((S + 1) % 3) * PB::kKC, tiles + ((S + 1) % 2) * PB::kT, PRE && kvis(s + 1) >= c.n_roll, false);
         if (cmp) {
-            const bool full = (kv != 0) && (rho + kTile <= c.rq + 1) && (s0 + kTile <= W);
+            const bool full =
+                vs.pre ? (s0 + kTile <= c.F) : ((kv != 0) && (rho + kTile <= c.rq + 1) && (s0 + kTile <= W));
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 if (w == 1 && !act1) break;
@@ -1518,8 +1646,10 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
                     for (int e = 0; e < 8; ++e) {
                         const int tt = 8 * gq + e;
                         const int r = rho + tt + ((seam & (tt < c.t_o)) ? W : 0);
-                        const bool ok = (r >= 0) & (r <= r_last) & ((rq_col[w] < 0) | (r <= rq_col[w])) &
-                                        (s0 + tt < W);
+                        const bool ok_ring = (r >= 0) & (r <= r_last) & ((rq_col[w] < 0) | (r <= rq_col[w])) &
+                                             (s0 + tt < W);
+                        const bool ok_pre = s0 + tt < c.F;      // prefix: before every query
+                        const bool ok = vs.pre ? ok_pre : ok_ring;
                         s8[e] = ok ? s8[e] : -INFINITY;
                     }
                 }
@@ -1640,6 +1770,14 @@ int pick_splits(int pairs, int tiles, int target_blocks, int min_tiles_per_split
     return sp;
 }
 
+// Whether any stream of the batch has a pinned prefix (selects the kernel
+// instance that walks prefix tiles).
+bool any_prefix(const StreamBatch& st) {
+    for (int i = 0; i < st.nb; ++i)
+        if (st.prefix[i] > 0) return true;
+    return false;
+}
+
 bool mfma_decode_ok(const Geometry& g) {
     return g.elem_bytes == 2 && g.group <= 16 && (g.d == 64 || g.d == 128);
 }
@@ -1661,9 +1799,12 @@ hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, 
                            int n_cu, const void* k_new, const void* v_new, hipStream_t s) {
     // one resident block per CU for D = 128 (one wave per SIMD), two for D = 64
     const int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, D == 128 ? n_cu : 2 * n_cu, 4);
-    hipLaunchKernelGGL((decode_mfma<D>), dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st,
-                       (const uint16_t*)q, (uint16_t*)out, n_split, (const uint16_t*)k_new,
-                       (const uint16_t*)v_new);
+    // three instances: the method, the method with a pinned prefix in the batch,
+    // and the rebase-on-evict variant (which has no prefix)
+    auto kern = g.prerot ? decode_mfma<D, true, false>
+              : any_prefix(st) ? decode_mfma<D, false, true> : decode_mfma<D, false, false>;
+    hipLaunchKernelGGL(kern, dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st, (const uint16_t*)q,
+                       (uint16_t*)out, n_split, (const uint16_t*)k_new, (const uint16_t*)v_new);
     return hipGetLastError();
 }
 
@@ -1673,8 +1814,9 @@ hipError_t run_chunk_pipe(const Geometry& g, int layer, const StreamBatch& st, i
     const int n_rg = (n_q * g.group + 127) / 128;      // row groups of up to 128 query rows
     const int n_split = pick_splits(st.nb * g.hkv * n_rg, g.w_pad / kTile, n_cu, 4);
     // two wave groups per block: two waves per SIMD
-    hipLaunchKernelGGL((chunk_pipe<D, NW, 2>), dim3(n_split * n_rg, g.hkv, st.nb), dim3(512), 0, s, g, layer, st,
-                       n_q, (const uint16_t*)q, (uint16_t*)out, n_split);
+    auto kern = any_prefix(st) ? chunk_pipe<D, NW, 2, true> : chunk_pipe<D, NW, 2, false>;
+    hipLaunchKernelGGL(kern, dim3(n_split * n_rg, g.hkv, st.nb), dim3(512), 0, s, g, layer, st, n_q,
+                       (const uint16_t*)q, (uint16_t*)out, n_split);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split == 1) return e;
     // the splits' partials are merged by a second, chip-wide kernel
@@ -1702,6 +1844,28 @@ hipError_t launch_append(const Geometry& g, int layer, const StreamBatch& before
     else
         hipLaunchKernelGGL(append_kernel<4>, dim3(before.nb), dim3(256), 0, s, g, layer, before, n_new,
                            (const uint8_t*)k, (const uint8_t*)v);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, const void* k,
+                                const void* v, hipStream_t s) {
+    if (g.elem_bytes == 2)
+        hipLaunchKernelGGL(prefix_append_kernel<2>, dim3(st.nb), dim3(256), 0, s, g, layer, st, n,
+                           (const uint8_t*)k, (const uint8_t*)v);
+    else
+        hipLaunchKernelGGL(prefix_append_kernel<4>, dim3(st.nb), dim3(256), 0, s, g, layer, st, n,
+                           (const uint8_t*)k, (const uint8_t*)v);
+    return hipGetLastError();
+}
+
+hipError_t launch_export_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, void* k, void* v,
+                                hipStream_t s) {
+    if (g.elem_bytes == 2)
+        hipLaunchKernelGGL(prefix_export_kernel<2>, dim3(st.nb), dim3(256), 0, s, g, layer, st, n, (uint8_t*)k,
+                           (uint8_t*)v);
+    else
+        hipLaunchKernelGGL(prefix_export_kernel<4>, dim3(st.nb), dim3(256), 0, s, g, layer, st, n, (uint8_t*)k,
+                           (uint8_t*)v);
     return hipGetLastError();
 }
 

@@ -60,12 +60,12 @@ class Twin:
     """One HIP cache and one oracle cache fed identical inputs."""
 
     def __init__(self, n_layers, n_streams, hq, hkv, d, window, max_chunk=1, bf16=True,
-                 portable=False, theta=1.0e6):
+                 portable=False, theta=1.0e6, prefix_capacity=0):
         self.shape = (n_layers, n_streams, hq, hkv, d, window)
         self.bf16 = bf16
         self.hq, self.hkv, self.d, self.window = hq, hkv, d, window
         self.cfg = a8r.make_config(n_layers, n_streams, hq, hkv, d, window, max_chunk, bf16, theta,
-                                   portable=portable)
+                                   portable=portable, prefix_capacity=prefix_capacity)
         self.gpu = a8r.Cache(self.cfg, stream=current_stream())
         self.ora = OracleCache(n_layers, n_streams, hq, hkv, d, window, theta)
         self.tol = TOL_BF16 if bf16 else TOL_F32
@@ -87,6 +87,18 @@ class Twin:
         assert np.array_equal(slots, np.array(s_ref, dtype=np.int32)), (slots, s_ref)
         assert np.array_equal(ev, np.array(e_ref, dtype=np.int64)), (ev, e_ref)
         return kd, vd
+
+    def append_prefix(self, layer, b0, k, v):
+        """k, v float32 [nb, n, Hkv, D]: pinned prefix tokens of streams b0 .. b0 + nb - 1."""
+        nb, n = k.shape[:2]
+        self.gpu.append_prefix(layer, b0, nb, n, to_device(k, self.bf16), to_device(v, self.bf16))
+        self.ora.append_prefix(layer, b0, k, v)
+        for i in range(nb):
+            assert self.gpu.prefix_length(layer, b0 + i) == self.ora.prefix_kv(layer, b0 + i)[0].shape[0]
+
+    def clear_prefix(self, b0, nb):
+        self.gpu.clear_prefix(b0, nb)
+        self.ora.clear_prefix(b0, nb)
 
     def check_state(self, layer, b):
         got = self.gpu.get_state(layer, b)

@@ -42,9 +42,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_config_struct_layout_matches_header():
-    # 10 int32 + double + 2 float = 40 + 8 + 8 = 56 bytes, double at offset 40
-    assert ctypes.sizeof(a8r.Config) == 56
+    # 10 int32 + double + 2 float + 2 int32 = 40 + 8 + 8 + 8 = 64 bytes, double at offset 40
+    assert ctypes.sizeof(a8r.Config) == 64
     assert a8r.Config.rope_theta.offset == 40
+    assert a8r.Config.prefix_capacity.offset == 56
 
 
 def test_version():
