@@ -7,7 +7,9 @@
  * Attention rotates keys and queries on read, by their index counted from the
  * window's current origin (the oldest live token), so query-key distances are
  * exact however large the absolute positions grow.  Stored K/V are never
- * modified after they are written.
+ * modified after they are written.  (K is written in tile-phase form, rotated
+ * once by its slot's offset in a 32-slot tile, which does not depend on the
+ * origin; see a8r_cache_mode.)
  *
  * Passages this interface follows:
  *  - "Audio8 ASR Infinite: What It Actually Takes to Listen Forever", flowchart
@@ -74,11 +76,18 @@ typedef enum a8r_kernel_policy { A8R_KERNELS_AUTO = 0, A8R_KERNELS_PORTABLE = 1 
 
 /* How stored keys carry their rotation.
  *
- * A8R_ROTATE_ON_READ (the method): K is stored exactly as appended and every
- * read rotates it by its re-based index ("Audio8 ASR Infinite: What It Actually
- * Takes to Listen Forever", section "Inside the Rolling KV Cache and Exact RoPE
- * Re-Basing": re-basing every surviving key to the new origin keeps relative
- * distances exact).  Stored bits never change, so nothing accumulates.
+ * A8R_ROTATE_ON_READ (the method): every read rotates a key by its re-based
+ * index ("Audio8 ASR Infinite: What It Actually Takes to Listen Forever",
+ * section "Inside the Rolling KV Cache and Exact RoPE Re-Basing": re-basing
+ * every surviving key to the new origin keeps relative distances exact).
+ * Stored bits never change, so nothing accumulates.  Storage form (tile-phase
+ * K): a key written to slot s is stored as R(s mod 32) k, computed in float32
+ * (multiplies and adds without fusion) and rounded once to the cache dtype
+ * (round to nearest even); values are stored as appended.  s mod 32 is fixed
+ * for the token's lifetime, so this is written once and never redone; a read
+ * at re-based index r = rho + (s mod 32) applies the remaining R(rho), which
+ * the kernels fold into the query.  Pinned prefix token j sits at slot
+ * offset j mod 32 the same way.
  *
  * A8R_REBASE_ON_EVICT (a comparison variant: the hazard the same page raises
  * there and in "Failure Modes That Only Appear on Day Three of a Session",
@@ -167,17 +176,23 @@ a8r_status a8r_reset(a8r_cache* cache, int32_t b0, int32_t nb, const int64_t* ne
  * Errors: EINVAL, ESTATE (ring not empty, poisoned), EUNSUPPORTED, EDEVICE. */
 a8r_status a8r_append_prefix(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb, int32_t n_new,
                              const void* k, const void* v);
-/* Export of a prepared prefix (the pages prepare a prefix once, as a separate
- * operation, and load it for every session; "Audio8-ASR-Infinite-Compressed",
- * Linux CPU notes).  Copies the n prefix tokens of streams [b0, b0+nb) in one
- * layer to k_out, v_out: device [nb][n][n_kv_heads][head_dim], 16-byte aligned,
- * the layout a8r_append_prefix takes, bit for bit as appended (so appending
- * them to another cache of the same shape and dtype imports the prefix).
- * Every stream in the range must hold exactly n >= 1 prefix tokens.
- * Asynchronous on the cache's stream.  Errors: EINVAL, ESTATE (poisoned),
- * EDEVICE. */
+/* Export and import of a prepared prefix (the pages prepare a prefix once, as
+ * a separate operation, bound to the build and its configuration, and load it
+ * for every session; "Audio8-ASR-Infinite-Compressed", Linux CPU notes).
+ * a8r_export_prefix copies the n prefix tokens of streams [b0, b0+nb) in one
+ * layer to k_out, v_out: device [nb][n][n_kv_heads][head_dim], 16-byte
+ * aligned, K in its storage form (tile-phase keys), V as appended.  Every
+ * stream in the range must hold exactly n >= 1 prefix tokens.
+ * a8r_import_prefix takes exactly that output (same head count, head_dim and
+ * dtype) and appends it to the prefixes of streams [b0, b0+nb) bit for bit;
+ * its preconditions and errors are a8r_append_prefix's.  An exported prefix
+ * imported at the same prefix offset (e.g. into empty prefixes) reproduces the
+ * original cache's stored bits.  Asynchronous on the cache's stream.
+ * Errors: EINVAL, ESTATE, EUNSUPPORTED, EDEVICE. */
 a8r_status a8r_export_prefix(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb, int32_t n,
                              void* k_out, void* v_out);
+a8r_status a8r_import_prefix(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb, int32_t n_new,
+                             const void* k, const void* v);
 a8r_status a8r_clear_prefix(a8r_cache* cache, int32_t b0, int32_t nb);
 /* Prefix length F of one (layer, stream) pair (host output). */
 a8r_status a8r_prefix_length(a8r_cache* cache, int32_t layer, int32_t b, int32_t* length);
@@ -240,8 +255,9 @@ a8r_status a8r_append_decode_attn(a8r_cache* cache, int32_t layer, int32_t b0, i
 a8r_status a8r_get_state(a8r_cache* cache, int32_t layer, int32_t b, int64_t* next_pos,
                          int32_t* length, int32_t* next_slot);
 
-/* Copy the raw ring of one (layer, stream) pair to host, in physical slot order
- * (with A8R_REBASE_ON_EVICT the K ring holds the rotated keys):
+/* Copy the ring of one (layer, stream) pair to host, in physical slot order, K
+ * in its storage form (tile-phase keys; with A8R_REBASE_ON_EVICT keys rotated
+ * to their index), V as appended:
  * k_host, v_host: host [W][n_kv_heads][head_dim] dtype elements (either may be
  * NULL).  Synchronizes the stream.  For tests and tooling. */
 a8r_status a8r_read_ring(a8r_cache* cache, int32_t layer, int32_t b, void* k_host, void* v_host);

@@ -28,9 +28,11 @@ attention  -- re-based decode / chunk attention over the live window, and the
 model      -- a whole cache (layers x streams) built from the three above.
 rebase     -- the rebase-on-evict comparison variant (keys stored rotated and
               re-rotated at every eviction, its float32/bf16 rounding emulated).
+storage    -- the storage form of keys in the ring (tile-phase K), for checking
+              ring contents bit for bit.
 
 Parity status of every function is pinned by tests under ``tests/`` marked
 ``not gpu``; none is "parity unpinned".
 """
 
-from . import ledger, rope, attention, model, rebase  # noqa: F401
+from . import ledger, rope, attention, model, rebase, storage  # noqa: F401

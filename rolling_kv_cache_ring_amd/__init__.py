@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ENOMEM", 3: "EDEVICE", 4: "ESTATE", 5:
 EXPORTED = [
     "a8r_workspace_bytes", "a8r_cache_create", "a8r_cache_destroy", "a8r_set_stream", "a8r_reset",
     "a8r_append_kv", "a8r_decode_attn", "a8r_chunk_attn", "a8r_append_decode_attn",
-    "a8r_get_state", "a8r_read_ring", "a8r_append_prefix", "a8r_export_prefix", "a8r_clear_prefix",
+    "a8r_get_state", "a8r_read_ring", "a8r_append_prefix", "a8r_export_prefix", "a8r_import_prefix", "a8r_clear_prefix",
     "a8r_prefix_length",
     "a8r_last_error", "a8r_ledger_create", "a8r_ledger_destroy", "a8r_ledger_reset",
     "a8r_ledger_append", "a8r_ledger_get", "a8r_version",
@@ -103,6 +103,9 @@ def lib():
     L.a8r_export_prefix.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     _c_void_p, _c_void_p]
     L.a8r_export_prefix.restype = st
+    L.a8r_import_prefix.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    _c_void_p, _c_void_p]
+    L.a8r_import_prefix.restype = st
     L.a8r_clear_prefix.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32]
     L.a8r_clear_prefix.restype = st
     L.a8r_prefix_length.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, _i32p]
@@ -289,6 +292,9 @@ class Cache:
 
     def export_prefix(self, layer, b0, nb, n, k_out, v_out):
         _check(lib().a8r_export_prefix(self.handle, layer, b0, nb, n, _ptr(k_out), _ptr(v_out)))
+
+    def import_prefix(self, layer, b0, nb, n_new, k, v):
+        _check(lib().a8r_import_prefix(self.handle, layer, b0, nb, n_new, _ptr(k), _ptr(v)))
 
     def clear_prefix(self, b0, nb):
         _check(lib().a8r_clear_prefix(self.handle, b0, nb))

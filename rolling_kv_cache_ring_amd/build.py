@@ -5,6 +5,12 @@
 Every HIP translation unit is compiled with packed-FP32 instruction selection
 disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``); hipcc's host
 pass prints a harmless warning that it does not know that feature.
+
+``-mllvm -amdgpu-mfma-vgpr-form=1`` makes the backend give MFMA results and
+accumulators VGPRs.  Without it the decode kernel's PV accumulators (updated
+by VALU in the online softmax) lived in VGPRs while each MFMA wrote an AGPR,
+so every visit copied them across and back (about 200 extra instructions per
+two visits); no kernel spills with it.
 """
 
 from __future__ import annotations
@@ -34,6 +40,7 @@ def command(out: str = LIB) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
 

@@ -506,8 +506,8 @@ a8r_status a8r_append_decode_attn(a8r_cache* c, int32_t layer, int32_t b0, int32
     return ok();
 }
 
-a8r_status a8r_append_prefix(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_new, const void* k,
-                             const void* v) {
+static a8r_status append_prefix(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_new, const void* k,
+                                const void* v, bool encode) {
     a8r_status st = check_live(c);
     if (st != A8R_OK) return st;
     if ((st = check_streams(c, layer, b0, nb)) != A8R_OK) return st;
@@ -529,11 +529,21 @@ a8r_status a8r_append_prefix(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb
         a8r::StreamBatch sb;
         fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
         hipError_t e = a8r::launch_append_prefix(c->geo, layer, sb, n_new, (const uint8_t*)k + i0 * row,
-                                                 (const uint8_t*)v + i0 * row, c->stream);
+                                                 (const uint8_t*)v + i0 * row, encode, c->stream);
         if (e != hipSuccess) return device_fail(c, e, "prefix append kernel");
     }
     for (int32_t i = 0; i < nb; ++i) c->prefix[(size_t)layer * c->cfg.n_streams + b0 + i] += n_new;
     return ok();
+}
+
+a8r_status a8r_append_prefix(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_new, const void* k,
+                             const void* v) {
+    return append_prefix(c, layer, b0, nb, n_new, k, v, true);
+}
+
+a8r_status a8r_import_prefix(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_new, const void* k,
+                             const void* v) {
+    return append_prefix(c, layer, b0, nb, n_new, k, v, false);
 }
 
 a8r_status a8r_export_prefix(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n, void* k, void* v) {

@@ -89,8 +89,10 @@ hipError_t launch_reset(const Geometry& g, const StreamBatch& after, hipStream_t
 // the append evicted e tokens, every surviving key by R(-e), in place.
 hipError_t launch_rebase(const Geometry& g, int layer, const StreamBatch& before, int n, hipStream_t s);
 // Writes n tokens into the pinned prefix of a batch at prefix slots F .. F+n-1.
+// Appends n prefix tokens per stream: raw tokens tile-phase encoded (encode),
+// or keys already in that form (an import of a8r_export_prefix's output).
 hipError_t launch_append_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, const void* k,
-                                const void* v, hipStream_t s);
+                                const void* v, bool encode, hipStream_t s);
 // Copies the n prefix tokens of each stream out to k, v [nb][n][Hkv][D].
 hipError_t launch_export_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, void* k, void* v,
                                 hipStream_t s);

@@ -7,12 +7,15 @@
 // re-based index r and the query at index r_q are rotated (split-half RoPE,
 // "Audio8-ASR-Infinite-mlx", section "Requires a patched mlx-audio-swift";
 // theta from "Audio8-ASR-0.1B in audio.cpp", section "Architecture") on read;
-// the stored K/V bits are never rewritten.
+// the stored K/V bits are never rewritten.  K is stored in tile-phase form,
+// R(slot mod 32) k, written once (see phase_pair), so a read applies only the
+// origin-dependent rest of the rotation.
 //
 // Kernels:
 //   reset_kernel       device record of the per-pair state after a reset
-//   append_kernel      copies new K/V rows into their ring slots (one block per
-//                      stream) and records the new state
+//   append_kernel      writes new K/V rows into their ring slots (K in
+//                      tile-phase form; one block per stream) and records the
+//                      new state
 //   attn_portable      any dtype / group size / chunk size; LDS-tiled VALU
 //   combine_kernel     merges split-K partials {m, l, O} of attn_portable,
 //                      and chunk_pipe
@@ -131,10 +134,58 @@ __device__ __forceinline__ void write_token_vals(const Geometry& g, int64_t pair
     store_token<EB>(g.k_ring, g.v_ring, g.pair_slots, g.d, pair, slot, c, kv, vv);
 }
 
+// Tile-phase storage of K.  A key written to slot s is stored as R(s mod 32) k:
+// rotated once, when it is written, by its offset in its 32-slot tile, and never
+// touched again.  A reader that visits the tile with base index rho (the key's
+// re-based index is rho + (s mod 32), plus W for a key behind the oldest slot on
+// the seam tile) then needs only R(rho), which it can apply to the query, since
+// <R(a) q, R(rho) R(t) k> = <R(a - rho) q, R(t) k>.  The stored value is the
+// rotation's exact float32 result rounded once to the cache dtype, the same
+// rounding a reader applies when it rotates a raw key into an MFMA operand.
+// Pairs (x1, x2) = dims (i, i + D/2) with (c, s) = table row t, pair i:
+// float32 multiplies and adds, no contraction (so every path and a float32
+// model of it store the same bits).
+__device__ __forceinline__ float2 phase_pair(float x1, float x2, float2 cs) {
+#pragma clang fp contract(off)
+    const float a = x1 * cs.x, b = x2 * cs.y, c = x2 * cs.x, d = x1 * cs.y;
+    return float2{a - b, c + d};
+}
+
+// Encodes the 16-byte K chunks lo (dims c*per16 ..) and hi (the same dims + D/2)
+// of one key with the pairs of table row `row` (a float2 row of D/2 pairs).
 template <int EB>
-__device__ __forceinline__ void write_token(const Geometry& g, int64_t pair, int slot, int c,
-                                            const uint8_t* ksrc, const uint8_t* vsrc) {
-    write_token_vals<EB>(g, pair, slot, c, *(const u32x4*)ksrc, *(const u32x4*)vsrc);
+__device__ __forceinline__ void encode_chunks(const float2* row, int c, u32x4& lo, u32x4& hi) {
+    if constexpr (EB == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float2 p0 = phase_pair(lo_bf16(lo[w]), lo_bf16(hi[w]), row[8 * c + 2 * w]);
+            const float2 p1 = phase_pair(hi_bf16(lo[w]), hi_bf16(hi[w]), row[8 * c + 2 * w + 1]);
+            lo[w] = (uint32_t)f32_to_bf16_bits(p0.x) | ((uint32_t)f32_to_bf16_bits(p1.x) << 16);
+            hi[w] = (uint32_t)f32_to_bf16_bits(p0.y) | ((uint32_t)f32_to_bf16_bits(p1.y) << 16);
+        }
+    } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float2 p = phase_pair(__uint_as_float(lo[w]), __uint_as_float(hi[w]), row[4 * c + w]);
+            lo[w] = __float_as_uint(p.x);
+            hi[w] = __float_as_uint(p.y);
+        }
+    }
+}
+
+// Writes token row j of the input ([nb][n][Hkv][D]) to `slot` of a pair: the
+// thread's K chunk c and its partner c + chunks/2 (tile-phase encoded unless
+// the keys are stored rotated to their index, A8R_REBASE_ON_EVICT), and the
+// same two V chunks as they are.
+template <int EB>
+__device__ __forceinline__ void write_token_pair(const Geometry& g, int64_t pair, int slot, int c, bool encode,
+                                                 const uint8_t* krow, const uint8_t* vrow) {
+    constexpr int per16 = 16 / EB;
+    const int half = g.d / per16 / 2;
+    u32x4 lo = *(const u32x4*)(krow + c * 16), hi = *(const u32x4*)(krow + (c + half) * 16);
+    if (encode) encode_chunks<EB>(g.table + (int64_t)(slot & (kTile - 1)) * (g.d / 2), c, lo, hi);
+    write_token_vals<EB>(g, pair, slot, c, lo, *(const u32x4*)(vrow + c * 16));
+    write_token_vals<EB>(g, pair, slot, c + half, hi, *(const u32x4*)(vrow + (c + half) * 16));
 }
 
 // One block per stream; token j of stream b goes to slot (S + j) mod W.
@@ -145,15 +196,15 @@ __global__ __launch_bounds__(256) void append_kernel(Geometry g, int layer, Stre
     const int bi = blockIdx.x, b = st.b0 + bi;
     const int D = g.d, W = g.window;
     constexpr int per16 = 16 / EB;
-    const int chunks = D / per16;
-    const int total = n_new * g.hkv * chunks;
+    const int halfc = D / per16 / 2;                   // chunk pairs per key
+    const int total = n_new * g.hkv * halfc;
     const int s0 = st.next_slot[bi];
     for (int t = threadIdx.x; t < total; t += blockDim.x) {
-        const int c = t % chunks;
-        const int rest = t / chunks;
+        const int c = t % halfc;
+        const int rest = t / halfc;
         const int kh = rest % g.hkv, j = rest / g.hkv;
-        const int64_t src = ((((int64_t)bi * n_new + j) * g.hkv + kh) * D + (int64_t)c * per16) * EB;
-        write_token<EB>(g, pair_index(g, layer, b, kh), wrap_slot(s0 + j, W), c, k + src, v + src);
+        const int64_t src = (((int64_t)bi * n_new + j) * g.hkv + kh) * D * EB;
+        write_token_pair<EB>(g, pair_index(g, layer, b, kh), wrap_slot(s0 + j, W), c, !g.prerot, k + src, v + src);
     }
     if (threadIdx.x == 0) {
         DevState ns;
@@ -165,30 +216,33 @@ __global__ __launch_bounds__(256) void append_kernel(Geometry g, int layer, Stre
 }
 
 // Pinned prefix: token j of stream b goes to prefix slot F + j (pair slot
-// w_pad + F + j, after the ring; never evicted).
+// w_pad + F + j, after the ring; never evicted).  Raw tokens are tile-phase
+// encoded like the ring's (phase (F + j) mod 32, the slot's offset in its
+// tile, since w_pad is a multiple of 32); an import (encode = false) writes
+// keys already in that form, as a8r_export_prefix returns them.
 template <int EB>
 __global__ __launch_bounds__(256) void prefix_append_kernel(Geometry g, int layer, StreamBatch st, int n_new,
                                                             const uint8_t* __restrict__ k,
-                                                            const uint8_t* __restrict__ v) {
+                                                            const uint8_t* __restrict__ v, int encode) {
     const int bi = blockIdx.x, b = st.b0 + bi;
     const int D = g.d;
     constexpr int per16 = 16 / EB;
-    const int chunks = D / per16;
-    const int total = n_new * g.hkv * chunks;
+    const int halfc = D / per16 / 2;
+    const int total = n_new * g.hkv * halfc;
     const int f0 = st.prefix[bi];
     for (int t = threadIdx.x; t < total; t += blockDim.x) {
-        const int c = t % chunks;
-        const int rest = t / chunks;
+        const int c = t % halfc;
+        const int rest = t / halfc;
         const int kh = rest % g.hkv, j = rest / g.hkv;
-        const int64_t src = ((((int64_t)bi * n_new + j) * g.hkv + kh) * D + (int64_t)c * per16) * EB;
-        store_token<EB>(g.k_ring, g.v_ring, g.pair_slots, D, pair_index(g, layer, b, kh), g.w_pad + f0 + j, c,
-                        *(const u32x4*)(k + src), *(const u32x4*)(v + src));
+        const int64_t src = (((int64_t)bi * n_new + j) * g.hkv + kh) * D * EB;
+        write_token_pair<EB>(g, pair_index(g, layer, b, kh), g.w_pad + f0 + j, c, encode != 0, k + src, v + src);
     }
 }
 
 // Export of a pinned prefix: prefix token j of stream b back to row j of the
-// append layout [nb][n][Hkv][D] (the inverse of prefix_append_kernel: K rows as
-// stored, V gathered back out of its transposed 8-slot blocks).
+// append layout [nb][n][Hkv][D]: K rows as stored (tile-phase encoded), V
+// gathered back out of its transposed 8-slot blocks.  An import
+// (prefix_append_kernel without encoding) restores exactly these bits.
 template <int EB>
 __global__ __launch_bounds__(256) void prefix_export_kernel(Geometry g, int layer, StreamBatch st, int n,
                                                             uint8_t* __restrict__ k, uint8_t* __restrict__ v) {
@@ -330,7 +384,9 @@ hipError_t launch_combine(const Geometry& g, int nb, int n_q, int n_split, void*
 // Block = (split of the key range, KV head, stream) x (group of 64 query rows).
 // Rows are (query c, head-in-group hg) = c * G + hg.  Keys are walked in
 // re-based order r = 0 .. L-1 (slot = (oldest + r) mod W) in tiles of 16; each
-// tile's K rows are rotated by R(r) into LDS; scores, online softmax and PV run
+// tile's K rows are rotated to R(r) into LDS (a stored key already carries
+// R(slot mod 32), so it takes R(r - slot mod 32), the conjugate of row
+// |r - slot mod 32| when that is negative); scores, online softmax and PV run
 // on VALU with 4 threads per row (4 keys of the tile each for the scores, a
 // quarter of the head dims each for PV).
 template <int D, int EB>
@@ -392,22 +448,15 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
         for (int idx = tid; idx < KT * NP; idx += 256) {
             const int j = idx / NP, i = idx - j * NP, r = kt * KT + j - F;
             float k1 = 0.f, k2 = 0.f, v1 = 0.f, v2 = 0.f;
-            if (r < 0) {                       // prefix token r + F at index r: R(r) = R(-r) conjugated
-                const int jp = g.w_pad + r + F;
-                const float x1 = load_elem<EB>(kring, (int64_t)jp * D + i);
-                const float x2 = load_elem<EB>(kring, (int64_t)jp * D + i + NP);
-                const float2 cs = g.table[(int64_t)(-r) * NP + i];
-                k1 = x1 * cs.x + x2 * cs.y;
-                k2 = x2 * cs.x - x1 * cs.y;
-                const int64_t vb = (int64_t)(jp >> 3) * D * 8 + (jp & 7);
-                v1 = load_elem<EB>(vring, vb + (int64_t)i * 8);
-                v2 = load_elem<EB>(vring, vb + (int64_t)(i + NP) * 8);
-            } else if (r < L) {
-                const int slot = wrap_slot(oldest + r, W);
+            if (r < L) {
+                // prefix token r + F (r < 0) at pair slot w_pad + r + F, else a ring slot
+                const int slot = r < 0 ? g.w_pad + r + F : wrap_slot(oldest + r, W);
                 const float x1 = load_elem<EB>(kring, (int64_t)slot * D + i);
                 const float x2 = load_elem<EB>(kring, (int64_t)slot * D + i + NP);
-                // keys stored already rotated (A8R_REBASE_ON_EVICT) are used as they are
-                const float2 cs = g.prerot ? float2{1.f, 0.f} : g.table[(int64_t)r * NP + i];
+                // keys stored rotated to their index (A8R_REBASE_ON_EVICT) are used as they are
+                const int e = r - (slot & (kTile - 1));
+                float2 cs = g.prerot ? float2{1.f, 0.f} : g.table[(int64_t)(e < 0 ? -e : e) * NP + i];
+                if (e < 0) cs.y = -cs.y;
                 k1 = x1 * cs.x - x2 * cs.y;
                 k2 = x2 * cs.x + x1 * cs.y;
                 const int64_t vb = (int64_t)(slot >> 3) * D * 8 + (slot & 7);
@@ -481,14 +530,15 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 //
 // Rotation: with R(x) the split-half rotation by index x, the score is
 // <R(r_q) q, R(rho + t) k> = <R(r_q - rho) q, R(t) k> because rotations in each
-// 2-D plane compose additively and are orthogonal.  Each lane always handles
-// the same two key offsets t of a tile, so its R(t) coefficients stay in
-// registers for the whole walk; the query is rotated once per visit by
+// 2-D plane compose additively and are orthogonal.  The ring stores R(t) k
+// (tile-phase form, written once by the append), so the visit's keys are MFMA
+// operands as they are, and only the query is rotated, once per visit, by
 // R(r_q - rho), a table row (< W + 32) fetched with the visit's keys.  On the
-// first visit the newest keys (offsets before the oldest slot) use
-// R(t + W) = R(W) R(t), composed in float32 from the R(W) row.  Every
-// coefficient comes from the float64-built table; no absolute position enters
-// float arithmetic.
+// first visit the newest keys (offsets before the oldest slot, index
+// rho + t + W) take a second query rotation R(r_q - rho - W), composed in
+// float32 from that row and the R(W) row, and their scores are selected from
+// it.  Every coefficient comes from the float64-built table; no absolute
+// position enters float arithmetic.
 //
 // MFMA mapping (v_mfma_f32_16x16x32_bf16, lane l = 16*gq + n):
 //   QK: S^T[key][head] = K_rot[key][dims] * Q_rot^T; A row n of tile half b is
@@ -694,25 +744,10 @@ __device__ __forceinline__ void dec_load_v(const DecodeCtx& c, int k, unsigned c
     for (int nb = 0; nb < D / 16; ++nb) dma16(vb + (int64_t)nb * 16 * 8, vbuf + nb * 1024);
 }
 
-// Coefficients of R(t + W) = R(W) R(t) where `wrap` (the lane's key offset lies
-// before the oldest slot on the first visit), else R(t).
-template <int D>
-__device__ __forceinline__ void seam_coef(const float4 (&rw)[D / 64][4], const float4 (&cf)[D / 64][4], bool wrap,
-                                          float4 (&out)[D / 64][4]) {
-#pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 a = cf[kk][j], w = rw[kk][j];
-            const float4 comp = {a.x * w.x - a.y * w.y, a.y * w.x + a.x * w.y,
-                                 a.z * w.z - a.w * w.w, a.w * w.z + a.z * w.w};
-            out[kk][j] = wrap ? comp : a;
-        }
-}
-
 // A visit's K part copied from LDS into registers: the query-rotation pairs
 // R(r_q - rho) and the lane's two K rows (tb0, tb1; dims 8*gq + 32*kk + e), so
-// that the buffer can be refilled before the arithmetic starts.
+// that the buffer can be refilled before the arithmetic starts.  The rows are
+// MFMA operands as they are: a stored key already carries R(t).
 template <int D>
 struct DecK {
     float4 qc[D / 64][4];
@@ -733,26 +768,57 @@ __device__ __forceinline__ void dec_read_k(const DecodeCtx& c, const unsigned ch
 
 // Scores of visit k from its K part and the online-softmax update; returns
 // this lane's eight probabilities (keys 8*gq .. 8*gq+7, head n) as bf16.
-template <int D>
+// SEAM: k may be the ring's first visit (only a wave's first visit can be).
+template <int D, bool SEAM>
 __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const DecK<D>& r,
-                                             const u32x4 (&qraw)[D / 32], const float4 (&cf0)[D / 64][4],
-                                             const float4 (&cf1)[D / 64][4], floatx4 (&o)[D / 16], float& m,
-                                             float& l) {
+                                             const u32x4 (&qraw)[D / 32], const unsigned char* lds_rw,
+                                             floatx4 (&o)[D / 16], float& m, float& l) {
     constexpr int KK = D / 32, NB = D / 16;
     const VisitSrc vs = visit_src(c, k);
     const int s0 = vs.s0, rho = vs.rho;
     bf16x8 qb[KK];
     rotate_row<D>(r.qc, qraw, qb);            // query by R(r_q - rho)
-    const bool seam = (k == 0) && (c.t_o > 0);
+    const bool seam = SEAM && (k == 0) && (c.t_o > 0);
     floatx4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
-    {
-        bf16x8 kb[KK];
-        rotate_row<D>(cf0, r.k0, kb);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], sc0, 0, 0, 0);
-        rotate_row<D>(cf1, r.k1, kb);
+    for (int kk = 0; kk < KK; ++kk) {
+        sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k0[kk]), qb[kk], sc0, 0, 0, 0);
+        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k1[kk]), qb[kk], sc1, 0, 0, 0);
+    }
+    if (seam && !c.prerot) {
+        // the seam visit (wave-uniform): keys behind the oldest slot sit W
+        // further on, so they take the query rotated by R(r_q - rho - W)
+        // (composed pair by pair from R(r_q - rho) and the R(W) row in LDS)
+        bf16x8 qbw[KK];
+        {
+            constexpr int HP = D / 64;
+            const float4* wrow = (const float4*)lds_rw + 4 * c.gq;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], sc1, 0, 0, 0);
+            for (int kk = 0; kk < HP; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float4 a4 = r.qc[kk][e >> 1], w4 = wrow[16 * kk + (e >> 1)];
+                    const float ax = (e & 1) ? a4.z : a4.x, ay = (e & 1) ? a4.w : a4.y;
+                    const float wx = (e & 1) ? w4.z : w4.x, wy = (e & 1) ? w4.w : w4.y;
+                    const float cx = ax * wx + ay * wy, cy = ay * wx - ax * wy;
+                    const uint32_t u1 = qraw[kk][e >> 1], u2 = qraw[kk + HP][e >> 1];
+                    const float x1 = (e & 1) ? hi_bf16(u1) : lo_bf16(u1);
+                    const float x2 = (e & 1) ? hi_bf16(u2) : lo_bf16(u2);
+                    qbw[kk][e] = (__bf16)(x1 * cx - x2 * cy);
+                    qbw[kk + HP][e] = (__bf16)(x2 * cx + x1 * cy);
+                }
+        }
+        floatx4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            w0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k0[kk]), qbw[kk], w0, 0, 0, 0);
+            w1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k1[kk]), qbw[kk], w1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {                 // element j: keys 8 gq + j and 8 gq + 4 + j
+            sc0[j] = 8 * c.gq + j < c.t_o ? w0[j] : sc0[j];
+            sc1[j] = 8 * c.gq + 4 + j < c.t_o ? w1[j] : sc1[j];
+        }
     }
     const float sl = c.scale_log2;
     float s[8] = {sc0[0] * sl, sc0[1] * sl, sc0[2] * sl, sc0[3] * sl,
@@ -842,12 +908,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     constexpr int KK = D / 32, NB = D / 16;
     using B = DecBuf<D>;
     // per wave: buffer a and b, each a K part and a V part, four distinct LDS
-    // objects; then the block's R(t) rows (t < 32), query rows and R(W) row
+    // objects; then the block's query rows, R(W) row and new token
     __shared__ __align__(16) unsigned char lds_ka[4 * B::kK];
     __shared__ __align__(16) unsigned char lds_va[4 * B::kV];
     __shared__ __align__(16) unsigned char lds_kb[4 * B::kK];
     __shared__ __align__(16) unsigned char lds_vb[4 * B::kV];
-    __shared__ __align__(16) unsigned char lds_rt[kTile * D * 4];
     __shared__ __align__(16) unsigned char lds_q[4096];
     __shared__ __align__(16) unsigned char lds_rw[1024];
     __shared__ __align__(16) unsigned char lds_tok[1024];
@@ -909,10 +974,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     const int k0 = split * per, k1 = min(n_visit, k0 + per);
 
     // Fused append: the wave whose visits include the new token's tile (visit
-    // k_tok) loads the token into LDS with its prologue, patches it into its LDS
-    // copy of that tile once the tile has landed, and writes it into the ring
-    // slot after the walk, so nothing waits for a store (no other wave or block
-    // reads that slot in this call).
+    // k_tok) loads the token into LDS with its prologue, tile-phase encodes its
+    // K row there, patches it into its LDS copy of that tile once the tile has
+    // landed, and writes it into the ring slot after the walk, so nothing waits
+    // for a store (no other wave or block reads that slot in this call).
     int k_tok = -1;
     const int t_tok = s_prev & (kTile - 1);
     if (fused) {
@@ -920,26 +985,24 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         if (kv < 0) kv += c.n_tiles;
         if (kv >= k0 && kv < k1 && (kv - k0) % 4 == wave) {
             // at most one wave per block: the token's K row to lds_tok[0, 2D),
-            // its V row to [2D, 4D) (other lanes re-read the K row's start)
+            // its V row to [2D, 4D), table row t_tok to [4D, 8D) (other lanes
+            // re-read the K row's start)
             k_tok = kv;
             const int64_t src = ((int64_t)bi * g.hkv + kh) * D;
-            const uint16_t* from = lane < D / 8 ? k_new + src + 8 * lane
-                                 : lane < D / 4 ? v_new + src + 8 * (lane - D / 8) : k_new + src;
+            const void* from = lane < D / 8   ? (const void*)(k_new + src + 8 * lane)
+                             : lane < D / 4   ? (const void*)(v_new + src + 8 * (lane - D / 8))
+                             : lane < D / 2   ? (const void*)((const unsigned char*)(g.table + (int64_t)t_tok * (D / 2)) +
+                                                              16 * (lane - D / 4))
+                                              : (const void*)(k_new + src);
             dma16(from, lds_tok + 16 * lane);
         }
     }
 
     // Prologue, every load a direct global->LDS load (so the explicit wait
-    // counts are exact): a quarter of the R(t) rows, a quarter of the query
-    // block (clamped to it), the R(W) row (wave 0), ...
+    // counts are exact): a quarter of the query block (clamped to it), the
+    // R(W) row (wave 0), ...
     int k = k0 + wave;
     {
-        constexpr int kRt = kTile * D * 4 / 1024 / 4;     // R(t) instructions per wave
-#pragma unroll
-        for (int j = 0; j < kRt; ++j) {
-            const int off = (wave * kRt + j) * 1024;
-            dma16((const unsigned char*)g.table + off + 16 * lane, lds_rt + off);
-        }
         const int qbytes = G * D * 2;
         int qo = wave * 1024 + 16 * lane;
         qo = qo < qbytes ? qo : qbytes - 16;
@@ -966,19 +1029,18 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
 
     // the query stays as bf16 bits (the softmax scale is applied to the scores)
     u32x4 qraw[KK];
-    float4 cf0[D / 64][4], cf1[D / 64][4];
     {
         const unsigned char* qrow = lds_q + (n < G ? n : 0) * D * 2 + 16 * gq;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qraw[kk] = *(const u32x4*)(qrow + 64 * kk);
-        lds_coef<D>(lds_rt + c.tb0 * D * 4, gq, cf0);
-        lds_coef<D>(lds_rt + c.tb1 * D * 4, gq, cf1);
-        if (c.prerot) {                  // keys already rotated: R(t) is the identity
-#pragma unroll
-            for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) cf0[kk][j] = cf1[kk][j] = float4{1.f, 0.f, 1.f, 0.f};
-        }
+    }
+    // the new token's K row in tile-phase form R(t_tok) k (the wave that owns it)
+    if (k_tok >= 0 && !c.prerot && lane < D / 16) {
+        u32x4* tk = (u32x4*)lds_tok;
+        u32x4 lo = tk[lane], hi = tk[lane + D / 16];
+        encode_chunks<2>((const float2*)(lds_tok + 4 * D), lane, lo, hi);
+        tk[lane] = lo;
+        tk[lane + D / 16] = hi;
     }
 
     floatx4 o[NB];
@@ -1014,16 +1076,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         dec_read_k<D>(c, ka, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);                                 // copied out of ka
         if (k + 8 < k1) dec_load_k<D>(c, k + 8, lane, ka);
-        bf16x8 pb;
-        if (k == 0 && c.t_o > 0 && !c.prerot) {   // the seam visit (a wave-uniform branch)
-            float4 rw[D / 64][4], s0c[D / 64][4], s1c[D / 64][4];
-            lds_coef<D>(lds_rw, gq, rw);
-            seam_coef<D>(rw, cf0, c.tb0 < c.t_o, s0c);
-            seam_coef<D>(rw, cf1, c.tb1 < c.t_o, s1c);
-            pb = dec_scores<D>(c, k, rk, qraw, s0c, s1c, o, m, l);
-        } else {
-            pb = dec_scores<D>(c, k, rk, qraw, cf0, cf1, o, m, l);
-        }
+        bf16x8 pb = dec_scores<D, true>(c, k, rk, qraw, lds_rw, o, m, l);
         wait_v(k);
         if (k == k_tok) patch_v<D>(va, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(va, lane, rv);
@@ -1037,7 +1090,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         dec_read_k<D>(c, kb, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         if (k + 8 < k1) dec_load_k<D>(c, k + 8, lane, kb);
-        pb = dec_scores<D>(c, k, rk, qraw, cf0, cf1, o, m, l);
+        pb = dec_scores<D, false>(c, k, rk, qraw, lds_rw, o, m, l);
         wait_v(k);
         if (k == k_tok) patch_v<D>(vb, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(vb, lane, rv);
@@ -1269,9 +1322,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
 // for the whole walk, and each wave issues a quarter of every visit's loads
 // (LDS DMA).
 // Rotation: each query row is rotated once, by its own re-based index
-// r_q(c) = L - C + c; key t of a visit by R(rho + t) = R(rho) R(t), R(rho) from
-// the table row staged with the visit, R(t) held by the lane (each lane always
-// rotates the same key offset and dims).  On the first visit rho = -t_o
+// r_q(c) = L - C + c; key t of a visit, stored as R(t) k (tile-phase form), by
+// R(rho), the table row staged with the visit.  On the first visit rho = -t_o
 // (R(t_o) conjugated), and the window's newest keys that share the oldest key's
 // tile (t < t_o, index t - t_o + W) get R(W) composed on top.  Query c sees
 // keys with index <= r_q(c): causal inside the chunk, the whole older window
@@ -1394,11 +1446,11 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         }
     };
 
-    // Prologue: register loads (query rows, the lane's R(t) pairs), R(W) into
-    // LDS (wave 0), the C consecutive table rows of the queries' rotations into
-    // LDS (1 KiB per wave, clamped to them), then K(0), K(1), V(0), issued even
-    // where those visits do not exist (then they re-read an in-range tile), so
-    // that the first wait below is unconditional.
+    // Prologue: register loads (query rows), R(W) into LDS (wave 0), the C
+    // consecutive table rows of the queries' rotations into LDS (1 KiB per
+    // wave, clamped to them), then K(0), K(1), V(0), issued even where those
+    // visits do not exist (then they re-read an in-range tile), so that the
+    // first wait below is unconditional.
     const int kr_t = 8 * wave + (lane >> 3);           // key offset this lane rotates
     const int kr_i = P * (lane & 7);                   // its first pair index
     u32x4 qr[NW][KK];
@@ -1410,16 +1462,6 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         const uint16_t* qp = q + (((int64_t)bi * C + cc) * g.hq + h) * D + 8 * gq;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qr[w][kk] = *(const u32x4*)(qp + 32 * kk);
-    }
-    float2 rt[P];
-    {
-        const float4* rp = (const float4*)(g.table + (int64_t)kr_t * (D / 2) + kr_i);
-#pragma unroll
-        for (int i = 0; i < P / 2; ++i) {
-            const float4 r4 = rp[i];
-            rt[2 * i] = float2{r4.x, r4.y};
-            rt[2 * i + 1] = float2{r4.z, r4.w};
-        }
     }
     if (wave_b == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
     {
@@ -1449,9 +1491,12 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     const int r_last = L - 1;
 
     // Rotates key kr_t of local visit v (pairs kr_i .. kr_i + P - 1) from its K
-    // slot into a rotated tile: R(rho + t) = R(rho) R(t); on the block's first
-    // visit of the ring (kv == 0) R(rho) = R(t_o) conjugated, and keys before
-    // the oldest slot (the window's newest) get R(W) on top.
+    // slot into a rotated tile.  The stored key already carries R(t) (tile-phase
+    // form), so it takes R(rho): the visit's staged row, conjugated where rho < 0
+    // (the ring's first visit, rho = -t_o, and prefix visits); on the first
+    // visit keys before the oldest slot (the window's newest) get R(W) on top.
+    // The rotated key is rounded to bf16 once more (the stored form was
+    // rounded once already).
     auto rotate = [&](const unsigned char* kslot, unsigned char* tile, bool first, bool seam) {
         const float4* br = (const float4*)(kslot + PB::kK) + kr_i / 2;
         const unsigned char* kraw = kslot + kr_t * D * 2;
@@ -1475,27 +1520,22 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
 #pragma unroll
         for (int i2 = 0; i2 < P / 2; ++i2) {
             const float4 b4 = br[i2];
-            const float2 bs[2] = {float2{b4.x, b4.y}, float2{b4.z, b4.w}};
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int i = 2 * i2 + h;
-                cf[i] = float2{bs[h].x * rt[i].x - bs[h].y * rt[i].y, bs[h].y * rt[i].x + bs[h].x * rt[i].y};
-            }
+            cf[2 * i2] = float2{b4.x, b4.y};
+            cf[2 * i2 + 1] = float2{b4.z, b4.w};
         }
-        if (first) {                                   // wave-uniform, first visit of the ring only
+        if (first) {                                   // wave-uniform: rho < 0
             const bool wrap = seam && kr_t < c.t_o;    // index kr_t - t_o + W: R(W) on top
             const float4* wr = (const float4*)lds_rw + kr_i / 2;
 #pragma unroll
             for (int i2 = 0; i2 < P / 2; ++i2) {
                 const float4 b4 = br[i2], w4 = wr[i2];
-                const float2 bs[2] = {float2{b4.x, -b4.y}, float2{b4.z, -b4.w}};
+                const float2 a2[2] = {float2{b4.x, -b4.y}, float2{b4.z, -b4.w}};
                 const float2 w2[2] = {float2{w4.x, w4.y}, float2{w4.z, w4.w}};
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int i = 2 * i2 + h;
-                    const float2 a = {bs[h].x * rt[i].x - bs[h].y * rt[i].y, bs[h].y * rt[i].x + bs[h].x * rt[i].y};
+                    const float2 a = a2[h];
                     const float2 r = {w2[h].x * a.x - w2[h].y * a.y, w2[h].y * a.x + w2[h].x * a.y};
-                    cf[i] = wrap ? r : a;
+                    cf[2 * i2 + h] = wrap ? r : a;
                 }
             }
         }
@@ -1848,13 +1888,13 @@ hipError_t launch_append(const Geometry& g, int layer, const StreamBatch& before
 }
 
 hipError_t launch_append_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, const void* k,
-                                const void* v, hipStream_t s) {
+                                const void* v, bool encode, hipStream_t s) {
     if (g.elem_bytes == 2)
         hipLaunchKernelGGL(prefix_append_kernel<2>, dim3(st.nb), dim3(256), 0, s, g, layer, st, n,
-                           (const uint8_t*)k, (const uint8_t*)v);
+                           (const uint8_t*)k, (const uint8_t*)v, encode ? 1 : 0);
     else
         hipLaunchKernelGGL(prefix_append_kernel<4>, dim3(st.nb), dim3(256), 0, s, g, layer, st, n,
-                           (const uint8_t*)k, (const uint8_t*)v);
+                           (const uint8_t*)k, (const uint8_t*)v, encode ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ import numpy as np
 import rolling_kv_cache_ring_amd as a8r
 import synth
 from oracle.model import OracleCache
+from oracle.storage import stored_keys
 
 TOL_F32 = 1e-5
 TOL_BF16 = 2e-2
@@ -147,12 +148,14 @@ class Twin:
         assert err <= self.tol, (what, err, self.tol)
 
     def check_ring(self, layer, b):
-        """Ring readback equals the oracle's physical ring on every live slot."""
+        """Ring readback equals the oracle's physical ring on every live slot,
+        bit for bit: V as appended, K in its storage form (oracle/storage.py)."""
         k, v = self.gpu.read_ring(layer, b)
         led = self.ora.ledger(layer, b)
         _, ring_k, ring_v = self.ora._pair(layer, b)
         live = [led.slot_of_live(j) for j in range(led.length)]
-        kk = synth.from_storage(k, self.bf16).astype(np.float64)
+        kk = synth.from_storage(k, self.bf16)
         vv = synth.from_storage(v, self.bf16).astype(np.float64)
-        assert np.array_equal(kk[live], ring_k[live])
+        exp_k = stored_keys(ring_k[live], np.array(live), self.bf16)
+        assert np.array_equal(kk[live].view(np.uint32), exp_k.view(np.uint32))
         assert np.array_equal(vv[live], ring_v[live])

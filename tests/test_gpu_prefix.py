@@ -12,8 +12,9 @@ in tests/test_oracle_prefix.py.  Covered here:
   of 2 .. 16 positions (several key splits at W = 512);
 * a prefix built by several appends; reset keeps the prefix, clear_prefix
   removes it, a new prefix after a reset;
-* export / import of a prepared prefix: the export equals the appended bits,
-  and a second cache importing it gives bitwise the same attention;
+* export / import of a prepared prefix: the export equals the stored form of
+  the appended tokens (oracle/storage.py: tile-phase K, V as appended), and a
+  second cache importing it gives bitwise the same attention;
 * ring readback unchanged by the prefix (the prefix lives past the ring);
 * errors: append to a non-empty window, beyond the capacity, a cache without
   prefix capacity, the rebase-on-evict mode.
@@ -23,7 +24,9 @@ import numpy as np
 import pytest
 
 import rolling_kv_cache_ring_amd as a8r
+import synth
 from gpu_util import Twin, say, to_device, empty_out, current_stream
+from oracle.storage import stored_keys
 
 pytestmark = pytest.mark.gpu
 
@@ -147,8 +150,11 @@ def test_prefix_export_import(bf16):
     a.append_prefix(1, 0, 3, f, kd, vd)
     ek, ev = torch.empty_like(kd), torch.empty_like(vd)
     a.export_prefix(1, 0, 3, f, ek, ev)
-    assert bool((ek == kd).all()) and bool((ev == vd).all())
-    b.append_prefix(1, 0, 3, f, ek, ev)                  # import
+    exp_k = stored_keys(pk, np.broadcast_to(np.arange(f), (3, f)), bf16)
+    got_k = synth.from_storage(ek.cpu().numpy().view(np.uint16) if bf16 else ek.cpu().numpy(), bf16)
+    assert np.array_equal(got_k.view(np.uint32), exp_k.view(np.uint32))
+    assert bool((ev == vd).all())
+    b.import_prefix(1, 0, 3, f, ek, ev)                  # import
     for c in (a, b):
         c.reset(0, [10, 2**24 - 7, 999], [3, 79, 40])
     outs = []
