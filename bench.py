@@ -12,7 +12,9 @@ through).  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps 1000] [--warmup 20] [--workload qwen3b_batch64]
 
 ``--workload qwen3b_chunk8`` measures the 8-position chunk path instead;
-``--prefix F`` pins an F-token prompt prefix in every (layer, stream) first.
+``--prefix F`` pins an F-token prompt prefix in every (layer, stream) first;
+``--workload qwen3b_single`` / ``audio8_0p1b`` time one stream (per-step
+latency of the 3B-class and the Audio8-0.1B decoder shapes).
 """
 
 from __future__ import annotations
@@ -42,7 +44,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="qwen3b_batch64", choices=["qwen3b_batch64", "qwen3b_chunk8", "qwen3b_chunk12", "qwen3b_chunk16"])
+    ap.add_argument("--workload", default="qwen3b_batch64",
+                    choices=["qwen3b_batch64", "qwen3b_chunk8", "qwen3b_chunk12", "qwen3b_chunk16",
+                             "qwen3b_single", "audio8_0p1b"])
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
                     help="decode step per layer as one a8r_append_decode_attn call (fused) or as "
                          "a8r_append_kv + a8r_decode_attn (separate)")
@@ -253,7 +257,10 @@ def main():
     cache = a8r.Cache(cfg, stream=stream.cuda_stream)
 
     # seeded start states; pre-fill each stream to min(P0, W) tokens ending at P0 - 1
+    # (the single-stream workloads start at P0 = 0: timed from a full window, P0 = W)
     p0, r0 = synth.start_states(wl)
+    if wl.n_streams == 1:
+        p0, r0 = p0 + w, (r0 + w) % w
     n_pre = np.minimum(p0, w)
     cache.reset(0, p0 - n_pre, (r0 - n_pre) % w)
     gen = torch.Generator(device="cuda")
@@ -382,7 +389,8 @@ def main():
         "config": {"workload": wl.name, "path": "fused" if fused else "separate",
                    "cache_mode": args.cache_mode, "layers": NL, "streams": B, "q_heads": hq, "kv_heads": hkv,
                    "head_dim": d, "window": w, "positions_per_step": c, "prefix": F,
-                   "start_positions": "seeded U[0,1e6)" if c == 1 else "seeded U[2^24-W,2^24)"},
+                   "start_positions": ("W (a full window)" if B == 1 else "seeded U[0,1e6)" if c == 1
+                                       else "seeded U[2^24-W,2^24)")},
         "kv_gbps": round(gbps_step, 1),
         "hbm_frac_step": round(gbps_step / HBM_PEAK_GBPS, 4),
         "bytes_per_step": bytes_step,

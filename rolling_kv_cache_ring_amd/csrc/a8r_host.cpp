@@ -115,8 +115,7 @@ struct Ledger {
 };
 
 struct Layout {
-    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, counter_off, part_t_off,
-        part_x_off, total;
+    size_t k_off, v_off, table_off, state_off, part_o_off, part_ml_off, part_x_off, total;
     int w_pad, f_pad, rows_max;
 };
 
@@ -182,16 +181,9 @@ a8r_status compute_layout(const a8r_config* c, Layout* lay) {
     off = a8r::align_up(off + prow * c->head_dim * 4, a8r::kAlign);
     lay->part_ml_off = off;
     off = a8r::align_up(off + prow * 2 * 4, a8r::kAlign);
-    lay->counter_off = off;
-    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * sizeof(int),
-                        a8r::kAlign);
-    lay->part_t_off = off;
-    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kMaxSplits * a8r::kMaxGroupTagged *
-                                  (c->head_dim + 2) * sizeof(uint64_t),
-                        a8r::kAlign);
     lay->part_x_off = off;
-    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kMaxGroupTagged * c->head_dim *
-                                  sizeof(uint64_t),
+    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kXSlots * a8r::kMaxGroupTagged *
+                                  c->head_dim * sizeof(uint64_t),
                         a8r::kAlign);
     lay->total = off;
     lay->w_pad = w_pad;
@@ -231,7 +223,6 @@ struct a8r_cache {
     a8r::Geometry geo{};
     hipStream_t stream = nullptr;
     void* base = nullptr;
-    mutable uint32_t epoch = 0;   // launch counter; tags decode split partials (never 0)
     std::vector<int32_t> prefix;  // pinned prefix length per (layer, stream)
     bool owns = false;
     bool poisoned = false;
@@ -327,8 +318,6 @@ a8r_status a8r_cache_create(const a8r_config* cfg, void* hip_stream, void* works
     g.state = (a8r::DevState*)(b + lay.state_off);
     g.part_o = (float*)(b + lay.part_o_off);
     g.part_ml = (float*)(b + lay.part_ml_off);
-    g.counters = (int*)(b + lay.counter_off);
-    g.part_t = (uint64_t*)(b + lay.part_t_off);
     g.part_x = (uint64_t*)(b + lay.part_x_off);
     g.n_layers = cfg->n_layers;
     g.n_streams = cfg->n_streams;
@@ -386,8 +375,6 @@ namespace {
 void fill_batch(const a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, a8r::StreamBatch* sb) {
     sb->b0 = b0;
     sb->nb = nb;
-    if (++c->epoch == 0) c->epoch = 1;   // the workspace starts zeroed: tag 0 never matches
-    sb->epoch = c->epoch;
     for (int32_t i = 0; i < nb; ++i) {
         const PairState& p = c->ledger.at(layer, b0 + i);
         sb->next_slot[i] = p.next_slot;

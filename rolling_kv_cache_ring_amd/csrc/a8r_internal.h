@@ -34,6 +34,7 @@ constexpr size_t kAlign = 256;
 constexpr int kBatch = 128;        // streams per launch (their state travels in the arguments)
 constexpr int kMaxGroupTagged = 16;   // query heads per KV head in the MFMA decode kernel
 constexpr uint64_t kSlotEmpty = ~(uint64_t)0;   // an exchange slot holding no partial
+constexpr int kXSlots = kMaxSplits - 1;         // exchange-slot rows per pair: the nodes of a merge tree
 
 struct DevState {
     int64_t next_pos;   // absolute position of the next token
@@ -45,7 +46,6 @@ struct DevState {
 // host bookkeeping holds it when the call is made.
 struct StreamBatch {
     int b0, nb;
-    uint32_t epoch;     // nonzero, different for every launch of a cache (tags split partials)
     int32_t next_slot[kBatch];
     int32_t length[kBatch];
     int32_t prefix[kBatch];   // pinned prefix length F (re-based indices 0 .. F-1; the window follows)
@@ -60,11 +60,8 @@ struct Geometry {
     DevState* state;
     float* part_o;      // split partials: [n_streams][n_kv_heads][kMaxSplits][rows_max][D]
     float* part_ml;     // [n_streams][n_kv_heads][kMaxSplits][rows_max][2]
-    int* counters;      // [n_streams][n_kv_heads] decode split arrival counters, 0 between calls
-    uint64_t* part_t;   // decode split partials tagged with the launch epoch (high word):
-                        // [n_streams][n_kv_heads][kMaxSplits][kMaxGroupTagged][D + 2] (O..., m, l)
-    uint64_t* part_x;   // two-split decode exchange slots, one per output element:
-                        // [n_streams][n_kv_heads][kMaxGroupTagged][D], kSlotEmpty between calls
+    uint64_t* part_x;   // decode merge-tree exchange slots, one per output element and tree node:
+                        // [kXSlots][n_streams][n_kv_heads][kMaxGroupTagged][D], kSlotEmpty between calls
     int n_layers, n_streams, hq, hkv, group, d, window, w_pad;
     int f_pad;          // prefix capacity rounded up to 32 (0: no prefix)
     int pair_slots;     // w_pad + f_pad: slots per (layer, stream, kv head)

@@ -21,8 +21,8 @@
 //                      and chunk_pipe
 //   decode_mfma        bf16 decode (optionally fused with the append of the
 //                      new token); QK^T and PV on v_mfma_f32_16x16x32_bf16,
-//                      split-K partials merged inside the kernel (two splits:
-//                      per-element atomic exchange; more: the last block)
+//                      split-K partials merged inside the kernel (a fixed
+//                      binary tree of per-element atomic exchanges)
 //   chunk_pipe         bf16 chunks of 2..16 positions (query rows of a KV head
 //                      in groups of up to 128 per block): keys rotated once
 //                      per visit into an LDS tile, QK^T and PV on MFMA,
@@ -560,9 +560,9 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 // vmcnt counts; the DMA destinations are hidden from the compiler's own wait
 // insertion (see opaque_lds), which would otherwise drain the queue.
 //
-// The splits of one (stream, KV head) publish {m, l, O} partials with
-// agent-coherent stores; the last block to arrive (agent-scope atomic counter)
-// merges them and re-arms the counter.
+// The splits of one (stream, KV head) merge their {m, l, O} partials per
+// output element through atomic-exchange slots arranged in a fixed binary tree
+// (see the end of the kernel).
 //
 // Fused append: with k_new != nullptr the state in the arguments is the state
 // before the append, the window is the one after it, and the wave that owns
@@ -899,6 +899,27 @@ __device__ __forceinline__ void patch_v(unsigned char* vbuf, int t, int lane, u3
     }
 }
 
+// A normalized split partial (o = O / l, lse = m + log2 l, base 2) packed in
+// 64 bits: lse in the high word, o in the low word.  A NaN lse is written as
+// the canonical quiet NaN, so a packed partial is never kSlotEmpty (all ones).
+__device__ __forceinline__ uint64_t pack_partial(float o, float lse) {
+    uint32_t hi = __float_as_uint(lse);
+    if (hi == 0xffffffffu) hi = 0x7fc00000u;
+    return ((uint64_t)hi << 32) | __float_as_uint(o);
+}
+
+// Merge of two packed partials, a first: weights 2^(lse - max); two empty
+// partials (lse = -inf) stay empty.
+__device__ __forceinline__ uint64_t merge_partials(uint64_t a, uint64_t b) {
+    const float la = __uint_as_float((uint32_t)(a >> 32)), lb = __uint_as_float((uint32_t)(b >> 32));
+    const float mx = fmaxf(la, lb);
+    if (mx == -INFINITY) return a;
+    const float wa = fast_exp2(la - mx), wb = fast_exp2(lb - mx);
+    const float sw = wa + wb;
+    const float o = (__uint_as_float((uint32_t)a) * wa + __uint_as_float((uint32_t)b) * wb) * __builtin_amdgcn_rcpf(sw);
+    return pack_partial(o, mx + __builtin_amdgcn_logf(sw));
+}
+
 template <int D, bool PREROT, bool PRE>
 __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, StreamBatch st,
                                                       const uint16_t* __restrict__ q,
@@ -917,7 +938,6 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     __shared__ __align__(16) unsigned char lds_rw[1024];
     __shared__ __align__(16) unsigned char lds_tok[1024];
     __shared__ float red_ml[4][16][2];
-    __shared__ int s_last;
     static_assert(4 * 16 * D * 4 <= 4 * B::kK, "merge buffer does not fit");
     float (*red_o)[16][D] = (float (*)[16][D])lds_ka;   // after the walk
 
@@ -1137,28 +1157,20 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
 
     // The block's partial {m, l, O} for each (head, dim) this thread owns.
     //
-    // Two splits (the usual case) meet per output element in an exchange slot
-    // that holds kSlotEmpty between calls: each swaps in its normalized partial
-    // (O / l, m + log2 l) with one 64-bit atomic exchange.  The one that gets the
-    // other's partial back (it came second) merges the element, writes the
-    // output and empties the slot; the one that gets kSlotEmpty back is done.
-    // One round trip, no block-wide count.
-    //
-    // More splits publish partials as (value, epoch) pairs with single 64-bit
-    // agent-coherent stores and count themselves in right away; the last block
-    // to arrive merges, re-reading any element whose tag is not yet this
-    // launch's (the stores are already in flight, so the wait is bounded).
-    //
-    // Either way the merge combines the splits in index order whichever block
-    // does it, so results are the same run to run.
+    // The splits of one (stream, KV head) merge per output element in a fixed
+    // binary tree: at each level the nodes 2m and 2m + 1 (splits at the first
+    // level; an odd last node passes up unchanged) meet in an exchange slot that
+    // holds kSlotEmpty between calls.  Each carrier swaps in its node's
+    // normalized partial (O / l, m + log2 l) with one 64-bit atomic exchange;
+    // the one that gets its partner's partial back (it came second) merges the
+    // two (node 2m always as the first operand), empties the slot and carries
+    // the result up; the one that gets kSlotEmpty back is done with that
+    // element.  Whoever carries it, a node's value is the same function of its
+    // children's, so results are the same run to run.  One round trip per
+    // level; two splits (the usual case) take one level and no block-wide
+    // count.
     constexpr int kPer = (kMaxGroupTagged * D + 255) / 256;
     float p_num[kPer], p_den[kPer], p_m[kPer];
-    uint64_t x_mine[kPer], x_old[kPer];
-    const uint32_t epoch = st.epoch;
-    auto tagged = [&](float x) { return ((uint64_t)epoch << 32) | __float_as_uint(x); };
-    auto trow = [&](int sp, int h) {
-        return g.part_t + ((((int64_t)bi * g.hkv + kh) * kMaxSplits + sp) * kMaxGroupTagged + h) * (D + 2);
-    };
     // elements of this thread: the same count across a wave (G * D is a
     // multiple of 64), so the loops below branch uniformly
     const int n_mine = __builtin_amdgcn_readfirstlane((G * D - 64 * wave + 255) / 256);
@@ -1187,130 +1199,78 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         }
         return;
     }
+    // slot rows node-major, [node][stream][kv head][head][D]: the first node's
+    // rows of all pairs (all that two splits use) are contiguous
+    const int64_t node_stride = (int64_t)g.n_streams * g.hkv * kMaxGroupTagged * D;
+    uint64_t* const slots = g.part_x + ((int64_t)bi * g.hkv + kh) * kMaxGroupTagged * D + tid;
     if (n_split == 2) {
-        uint64_t* slots = g.part_x + ((int64_t)bi * g.hkv + kh) * kMaxGroupTagged * D;
-        // every exchange issued before any result is needed
+        // one level: the same exchange written out (every exchange issued
+        // before any result is needed, the merge and the output store
+        // straight after)
+        uint64_t x_mine[kPer], x_old[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             if (i >= n_mine) break;
-            // an empty split (short window) has den = 0: weight 0 in the merge
-            const bool live = p_den[i] > 0.f;             // then den >= 1 (the max term is 1)
+            const bool live = p_den[i] > 0.f;
             const float on = live ? p_num[i] * __builtin_amdgcn_rcpf(p_den[i]) : 0.f;
-            uint32_t lse = __float_as_uint(live ? p_m[i] + __builtin_amdgcn_logf(p_den[i]) : -INFINITY);
-            if (lse == 0xffffffffu) lse = 0x7fc00000u;          // never kSlotEmpty
-            x_mine[i] = ((uint64_t)lse << 32) | __float_as_uint(on);
-            x_old[i] = __hip_atomic_exchange(slots + tid + 256 * i, x_mine[i], __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
+            x_mine[i] = pack_partial(on, live ? p_m[i] + __builtin_amdgcn_logf(p_den[i]) : -INFINITY);
+            x_old[i] = __hip_atomic_exchange(slots + 256 * i, x_mine[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             if (i >= n_mine) break;
-            const uint64_t other = x_old[i];
-            const bool second = other != kSlotEmpty;          // else the other split merges it
-            const uint64_t a = split == 0 ? x_mine[i] : other, c1 = split == 0 ? other : x_mine[i];
+            if (x_old[i] == kSlotEmpty) continue;             // the other split merges it
+            const uint64_t a = split == 0 ? x_mine[i] : x_old[i], c1 = split == 0 ? x_old[i] : x_mine[i];
             const float la = __uint_as_float((uint32_t)(a >> 32)), lb = __uint_as_float((uint32_t)(c1 >> 32));
             const float mx = fmaxf(la, lb);
             const float wa = fast_exp2(la - mx), wb = fast_exp2(lb - mx);
             const float r = (__uint_as_float((uint32_t)a) * wa + __uint_as_float((uint32_t)c1) * wb) *
                             __builtin_amdgcn_rcpf(wa + wb);
-            if (second) {
-                out_at(tid + 256 * i) = f32_to_bf16_bits(r);
-                __hip_atomic_store(slots + tid + 256 * i, kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            out_at(tid + 256 * i) = f32_to_bf16_bits(r);
+            __hip_atomic_store(slots + 256 * i, kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         return;
     }
+    // normalized partials; an empty split (short window) has den = 0 and
+    // enters as (0, -inf), weight 0 in every merge
+    uint64_t xv[kPer];
+    bool carry[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
+        carry[i] = i < n_mine;
         if (i >= n_mine) break;
-        const int idx = tid + 256 * i;
-        const int h = idx / D, d = idx - h * D;
-        uint64_t* pr = trow(split, h);
-        __hip_atomic_store(pr + d, tagged(p_num[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (d == 0) {
-            __hip_atomic_store(pr + D, tagged(p_m[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(pr + D + 1, tagged(p_den[i]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        const bool live = p_den[i] > 0.f;             // then den >= 1 (the max term is 1)
+        const float on = live ? p_num[i] * __builtin_amdgcn_rcpf(p_den[i]) : 0.f;
+        xv[i] = pack_partial(on, live ? p_m[i] + __builtin_amdgcn_logf(p_den[i]) : -INFINITY);
     }
-
-    __syncthreads();            // every store of the block has been issued
-    int* counter = &g.counters[bi * g.hkv + kh];
-    if (tid == 0) {
-        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == n_split - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    // Merge: splits in index order, an online combination per element
-    // (running max, numerator, denominator).  For each other split, the loads
-    // of all of this thread's elements are issued together; an element whose
-    // tag is not yet this launch's is re-read (its store is in flight).  A
-    // value that never arrives (impossible unless memory is corrupted) becomes
-    // NaN after a bounded number of retries instead of hanging.
-    float r_m[kPer], r_num[kPer], r_den[kPer];
+    int node = split, width = n_split, base = 0;   // wave-uniform
+    while (width > 1) {
+        if ((node ^ 1) < width) {
+            uint64_t* sl = slots + (base + (node >> 1)) * node_stride;
+            uint64_t old[kPer];
+            // every exchange of the level issued before any result is needed
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        r_m[i] = kNegBig;
-        r_num[i] = 0.f;
-        r_den[i] = 0.f;
-    }
-    for (int sp = 0; sp < n_split; ++sp) {
-        float vm[kPer], vl[kPer], vo[kPer];
-        if (sp == split) {
+            for (int i = 0; i < kPer; ++i)
+                if (carry[i]) old[i] = __hip_atomic_exchange(sl + 256 * i, xv[i], __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
-                vm[i] = p_m[i];
-                vl[i] = p_den[i];
-                vo[i] = p_num[i];
-            }
-        } else {
-            uint64_t tm[kPer], tl[kPer], to[kPer];
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                if (i >= n_mine) break;
-                const int idx = tid + 256 * i, h = idx / D, d = idx - h * D;
-                const uint64_t* pr = trow(sp, h);
-                tm[i] = __hip_atomic_load(pr + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                tl[i] = __hip_atomic_load(pr + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                to[i] = __hip_atomic_load(pr + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                if (i >= n_mine) break;
-                const int idx = tid + 256 * i, h = idx / D, d = idx - h * D;
-                const uint64_t* pr = trow(sp, h);
-                bool ok = false;
-                for (int spin = 0; spin < (1 << 16); ++spin) {
-                    ok = (uint32_t)(tm[i] >> 32) == epoch && (uint32_t)(tl[i] >> 32) == epoch &&
-                         (uint32_t)(to[i] >> 32) == epoch;
-                    if (ok) break;
-                    __builtin_amdgcn_s_sleep(1);
-                    tm[i] = __hip_atomic_load(pr + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    tl[i] = __hip_atomic_load(pr + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    to[i] = __hip_atomic_load(pr + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (!carry[i]) continue;
+                if (old[i] == kSlotEmpty) {            // the partner carries this element on
+                    carry[i] = false;
+                    continue;
                 }
-                vm[i] = __uint_as_float((uint32_t)tm[i]);
-                vl[i] = ok ? __uint_as_float((uint32_t)tl[i]) : __uint_as_float(0x7fc00000u);
-                vo[i] = __uint_as_float((uint32_t)to[i]);
+                xv[i] = (node & 1) ? merge_partials(old[i], xv[i]) : merge_partials(xv[i], old[i]);
+                __hip_atomic_store(sl + 256 * i, kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            if (i >= n_mine) break;
-            const float mn = fmaxf(r_m[i], vm[i]);
-            const float a = exp2f(r_m[i] - mn), f = exp2f(vm[i] - mn);
-            r_num[i] = r_num[i] * a + vo[i] * f;
-            r_den[i] = r_den[i] * a + vl[i] * f;
-            r_m[i] = mn;
-        }
+        base += width >> 1;
+        node >>= 1;
+        width = (width + 1) >> 1;
     }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        if (i >= n_mine) break;
-        const int idx = tid + 256 * i, h = idx / D, d = idx - h * D;
-        out[((int64_t)bi * g.hq + kh * G + h) * D + d] = f32_to_bf16_bits(r_num[i] / r_den[i]);
-    }
-    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < kPer; ++i)
+        if (carry[i]) out_at(tid + 256 * i) = f32_to_bf16_bits(__uint_as_float((uint32_t)xv[i]));
 }
 
 // ---------------------------------------------------------- pipelined chunk --
