@@ -182,7 +182,7 @@ a8r_status compute_layout(const a8r_config* c, Layout* lay) {
     lay->part_ml_off = off;
     off = a8r::align_up(off + prow * 2 * 4, a8r::kAlign);
     lay->part_x_off = off;
-    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kXSlots * a8r::kMaxGroupTagged *
+    off = a8r::align_up(off + (size_t)c->n_streams * c->n_kv_heads * a8r::kXSlots * a8r::kMaxGroupMfma *
                                   c->head_dim * sizeof(uint64_t),
                         a8r::kAlign);
     lay->total = off;

@@ -32,7 +32,7 @@ constexpr int kMaxSplits = 16;     // most key splits per (stream, KV head)
 constexpr int kMaxPartialQ = 16;   // chunk sizes above this run without splits
 constexpr size_t kAlign = 256;
 constexpr int kBatch = 128;        // streams per launch (their state travels in the arguments)
-constexpr int kMaxGroupTagged = 16;   // query heads per KV head in the MFMA decode kernel
+constexpr int kMaxGroupMfma = 16;   // query heads per KV head in the MFMA decode kernel
 constexpr uint64_t kSlotEmpty = ~(uint64_t)0;   // an exchange slot holding no partial
 constexpr int kXSlots = kMaxSplits - 1;         // exchange-slot rows per pair: the nodes of a merge tree
 
@@ -61,7 +61,7 @@ struct Geometry {
     float* part_o;      // split partials: [n_streams][n_kv_heads][kMaxSplits][rows_max][D]
     float* part_ml;     // [n_streams][n_kv_heads][kMaxSplits][rows_max][2]
     uint64_t* part_x;   // decode merge-tree exchange slots, one per output element and tree node:
-                        // [kXSlots][n_streams][n_kv_heads][kMaxGroupTagged][D], kSlotEmpty between calls
+                        // [kXSlots][n_streams][n_kv_heads][kMaxGroupMfma][D], kSlotEmpty between calls
     int n_layers, n_streams, hq, hkv, group, d, window, w_pad;
     int f_pad;          // prefix capacity rounded up to 32 (0: no prefix)
     int pair_slots;     // w_pad + f_pad: slots per (layer, stream, kv head)

@@ -717,10 +717,10 @@ __device__ __forceinline__ void dma_table_row(const float2* table, int row, int 
     dma16((const unsigned char*)(table + (int64_t)row * (D / 2)) + off, dst);
 }
 
-// The coefficient row staged after the K rows: R(r_q - rho) for decode (the
-// query's rotation for this visit); for the chunk kernel R(rho), or R(t_o) on
-// the first visit (rho = -t_o, used conjugated).
-template <int D, bool CHUNK = false>
+// The coefficient row staged after the K rows: R(r_q - rho), the query's
+// rotation for this visit (R(r_q) when the keys are stored rotated to their
+// index).
+template <int D>
 __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, unsigned char* kbuf) {
     constexpr int RPI = 64 / (D / 8);            // rows per instruction
     const VisitSrc vs = visit_src(c, k);
@@ -731,9 +731,7 @@ __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, 
         const int col = 8 * (sl >> 3) + ((sl & 7) ^ k_swz(r));
         dma16(c.kp + (int64_t)(vs.tile * kTile + r) * D + 8 * col, kbuf + j * 1024);
     }
-    const int rho = vs.rho;
-    dma_table_row<D>(c.table, CHUNK ? (rho < 0 ? -rho : rho) : c.rq - (c.prerot ? 0 : rho), lane,
-                     kbuf + 2 * (D / 32) * 1024);
+    dma_table_row<D>(c.table, c.rq - (c.prerot ? 0 : vs.rho), lane, kbuf + 2 * (D / 32) * 1024);
 }
 
 template <int D>
@@ -1169,7 +1167,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     // children's, so results are the same run to run.  One round trip per
     // level; two splits (the usual case) take one level and no block-wide
     // count.
-    constexpr int kPer = (kMaxGroupTagged * D + 255) / 256;
+    constexpr int kPer = (kMaxGroupMfma * D + 255) / 256;
     float p_num[kPer], p_den[kPer], p_m[kPer];
     // elements of this thread: the same count across a wave (G * D is a
     // multiple of 64), so the loops below branch uniformly
@@ -1201,8 +1199,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     }
     // slot rows node-major, [node][stream][kv head][head][D]: the first node's
     // rows of all pairs (all that two splits use) are contiguous
-    const int64_t node_stride = (int64_t)g.n_streams * g.hkv * kMaxGroupTagged * D;
-    uint64_t* const slots = g.part_x + ((int64_t)bi * g.hkv + kh) * kMaxGroupTagged * D + tid;
+    const int64_t node_stride = (int64_t)g.n_streams * g.hkv * kMaxGroupMfma * D;
+    uint64_t* const slots = g.part_x + ((int64_t)bi * g.hkv + kh) * kMaxGroupMfma * D + tid;
     if (n_split == 2) {
         // one level: the same exchange written out (every exchange issued
         // before any result is needed, the merge and the output store

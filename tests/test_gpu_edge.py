@@ -171,7 +171,7 @@ def test_errors_leave_state_unchanged():
 @pytest.mark.parametrize("streams,window", [(4, 512), (64, 256)])
 def test_bitwise_deterministic(portable, streams, window):
     """Repeated calls give identical bits: 4 streams take the multi-split merge
-    (epoch-tagged partials), 64 streams the two-split exchange."""
+    (the exchange tree over several levels), 64 streams the two-split exchange."""
     say("bitwise_deterministic", portable, streams, window)
     rng = np.random.default_rng(5)
     tw = Twin(1, streams, 16, 2, 128, window, 8, True, portable)
@@ -186,6 +186,31 @@ def test_bitwise_deterministic(portable, streams, window):
     for o in outs:
         tw.gpu.decode_attn(0, 0, streams, q, o)
     assert bool((outs[0] == outs[1]).all()) and bool((outs[0] == outs[2]).all())
+    tw.close()
+
+
+@pytest.mark.parametrize("window", [400, 700, 950, 1600])
+def test_decode_merge_tree_split_counts(window):
+    """One stream (two KV heads): the window is split 3, 5, 7 and 12 ways (about a
+    quarter of its 32-slot tiles, up to 16), so the merge tree has unpaired
+    nodes that pass up; parity through fills and a wrap, and identical bits on
+    repeated calls."""
+    say("decode_merge_tree", window)
+    rng = np.random.default_rng(window)
+    tw = Twin(1, 1, 16, 2, 128, window, 1, True)
+    tw.reset(0, [2**24 - window // 2], [window // 3])
+    for t in range(window + 40):
+        k, v = rand(rng, 1, 1, 2, 128), rand(rng, 1, 1, 2, 128)
+        if t % 97 == 0 or t >= window + 37:
+            tw.append_decode(0, 0, k, v, rand(rng, 1, 16, 128))
+        else:
+            tw.append(0, 0, k, v)
+    q = to_device(rand(rng, 1, 16, 128), True)
+    outs = [empty_out((1, 16, 128), True) for _ in range(3)]
+    for o in outs:
+        tw.gpu.decode_attn(0, 0, 1, q, o)
+    assert bool((outs[0] == outs[1]).all()) and bool((outs[0] == outs[2]).all())
+    say("worst err", tw.worst)
     tw.close()
 
 
