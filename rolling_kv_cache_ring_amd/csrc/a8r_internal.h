@@ -2,21 +2,26 @@
 // kernels (a8r_kernels.hip).  Not part of the public ABI.
 //
 // Device memory layout of one cache (all regions 256-byte aligned):
-//   K ring  [n_layers][n_streams][n_kv_heads][W_pad][D]        row per slot
-//   V ring  [n_layers][n_streams][n_kv_heads][W_pad/8][D][8]   8-slot blocks,
-//            transposed inside a block so 8 consecutive slots of one dim are
-//            16 contiguous bytes (the k-operand layout of the PV MFMA)
-//   table   [W + 32][D/2] float2: (cos, sin)(r * theta^(-2i/D)) for r < W + 32,
-//            built in float64 on the host and rounded once to float32
+//   K ring  [n_layers][n_streams][n_kv_heads][W_pad + F_pad][D]   row per slot:
+//            ring slots 0 .. W-1, then the pinned prefix from slot W_pad; a key
+//            is stored in tile-phase form R(slot mod 32) k (the rebase-on-evict
+//            variant: rotated to its re-based index)
+//   V ring  [n_layers][n_streams][n_kv_heads][(W_pad + F_pad)/8][D][8]   8-slot
+//            blocks, transposed inside a block so 8 consecutive slots of one dim
+//            are 16 contiguous bytes (the k-operand layout of the PV MFMA)
+//   table   [W + F_pad + 32][D/2] float2: (cos, sin)(r * theta^(-2i/D)), built
+//            in float64 on the host and rounded once to float32
 //   state   [n_layers][n_streams] DevState: a device-side record of every
 //            pair's (P, L, S), written by the reset / append kernels and read
 //            back only by a8r_get_state to cross-check the host bookkeeping.
 //            Kernels take the state they work on from their launch arguments
 //            (StreamBatch), filled from the host bookkeeping at call time.
-//   scratch split partials: O [rows][D] float32 and (m, l) [rows][2] float32,
-//            and one arrival counter per (stream, KV head), zero between calls
-// W_pad = W rounded up to a multiple of 32 (one MFMA key tile); padding slots
-// are zeroed at creation and never written, and never taken as live.
+//   scratch split partials: O [rows][D] float32 and (m, l) [rows][2] float32
+//            (chunk and portable kernels, merged by combine_kernel), and the
+//            decode merge tree's exchange slots, all ones between calls
+// W_pad = W rounded up to a multiple of 32 (one MFMA key tile); F_pad = the
+// prefix capacity rounded up to 32.  Padding slots are zeroed at creation, never
+// written, and never taken as live.
 #pragma once
 
 #include <stddef.h>
