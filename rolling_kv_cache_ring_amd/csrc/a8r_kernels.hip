@@ -683,6 +683,17 @@ __device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
     __builtin_amdgcn_global_load_lds(src, opaque_lds(lds_dst), 16, 0, 0);
 }
 
+// The same with the non-temporal cache policy (streaming data read once per
+// launch: the decode walk's K and V).  Its lines leave the L2 early, so the
+// small data every block re-reads (the rotation table rows, one per visit)
+// stays resident: the decode launch takes about 4.5 us less at the 64-stream
+// 3B shape.  The chunk kernel reads each K/V tile once per block too, but
+// gains nothing from it (within 0.1 us with K, V or both streaming).
+__device__ __forceinline__ void dma16_stream(const void* src, unsigned char* lds_dst) {
+    constexpr int kNonTemporal = 2;   // cache-policy bit NT of the load
+    __builtin_amdgcn_global_load_lds(src, opaque_lds(lds_dst), 16, 0, kNonTemporal);
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
 // 6:4, lgkmcnt in 11:8): "at most n vector-memory operations outstanding", and
 // "no LDS operation outstanding".
@@ -729,7 +740,7 @@ __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, 
     for (int j = 0; j < 2 * (D / 32); ++j) {
         const int r = RPI * j + rl;
         const int col = 8 * (sl >> 3) + ((sl & 7) ^ k_swz(r));
-        dma16(c.kp + (int64_t)(vs.tile * kTile + r) * D + 8 * col, kbuf + j * 1024);
+        dma16_stream(c.kp + (int64_t)(vs.tile * kTile + r) * D + 8 * col, kbuf + j * 1024);
     }
     dma_table_row<D>(c.table, c.rq - (c.prerot ? 0 : vs.rho), lane, kbuf + 2 * (D / 32) * 1024);
 }
@@ -739,7 +750,7 @@ __device__ __forceinline__ void dec_load_v(const DecodeCtx& c, int k, unsigned c
     const VisitSrc vs = visit_src(c, k);
     const uint16_t* vb = c.vp + ((int64_t)(vs.tile * 4 + c.gq) * D + c.n) * 8;
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) dma16(vb + (int64_t)nb * 16 * 8, vbuf + nb * 1024);
+    for (int nb = 0; nb < D / 16; ++nb) dma16_stream(vb + (int64_t)nb * 16 * 8, vbuf + nb * 1024);
 }
 
 // A visit's K part copied from LDS into registers: the query-rotation pairs
