@@ -947,8 +947,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     __shared__ __align__(16) unsigned char lds_rw[1024];
     __shared__ __align__(16) unsigned char lds_tok[1024];
     __shared__ float red_ml[4][16][2];
-    static_assert(4 * 16 * D * 4 <= 4 * B::kK, "merge buffer does not fit");
-    float (*red_o)[16][D] = (float (*)[16][D])lds_ka;   // after the walk
+    // rows padded by 4 floats: the float4 writes of a column group's 16 lanes
+    // (one row each) then spread over the banks
+    constexpr int kRow = D + 4;
+    static_assert(4 * 16 * kRow * 4 <= 4 * B::kK, "merge buffer does not fit");
+    float (*red_o)[16][kRow] = (float (*)[16][kRow])lds_ka;   // after the walk
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1158,8 +1161,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             if (gq == 0) red_ml[wave][n][1] = l * f;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) red_o[wave][n][16 * nb + 4 * gq + j] = o[nb][j] * f;
+                *(float4*)&red_o[wave][n][16 * nb + 4 * gq] =
+                    float4{o[nb][0] * f, o[nb][1] * f, o[nb][2] * f, o[nb][3] * f};
         }
     }
     __syncthreads();
