@@ -683,15 +683,18 @@ __device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
     __builtin_amdgcn_global_load_lds(src, opaque_lds(lds_dst), 16, 0, 0);
 }
 
-// The same with the non-temporal cache policy (streaming data read once per
-// launch: the decode walk's K and V).  Its lines leave the L2 early, so the
-// small data every block re-reads (the rotation table rows, one per visit)
-// stays resident: the decode launch takes about 4.5 us less at the 64-stream
-// 3B shape.  The chunk kernel reads each K/V tile once per block too, but
-// gains nothing from it (within 0.1 us with K, V or both streaming).
-__device__ __forceinline__ void dma16_stream(const void* src, unsigned char* lds_dst) {
+// The same with the non-temporal cache policy when STREAM (data read once per
+// launch and too large to stay cached until the next: the decode walk's K and
+// V at large batch).  Its lines leave the L2 early, so the small data every
+// block re-reads (the rotation table rows, one per visit) stays resident: the
+// decode launch takes about 4.5 us less at the 64-stream 3B shape.  A window
+// set that fits in the caches (one stream: the next step reads it again) is
+// better served by the default policy, and the chunk kernel gains nothing from
+// it (within 0.1 us with K, V or both streaming).
+template <bool STREAM>
+__device__ __forceinline__ void dma16_policy(const void* src, unsigned char* lds_dst) {
     constexpr int kNonTemporal = 2;   // cache-policy bit NT of the load
-    __builtin_amdgcn_global_load_lds(src, opaque_lds(lds_dst), 16, 0, kNonTemporal);
+    __builtin_amdgcn_global_load_lds(src, opaque_lds(lds_dst), 16, 0, STREAM ? kNonTemporal : 0);
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
@@ -731,7 +734,7 @@ __device__ __forceinline__ void dma_table_row(const float2* table, int row, int 
 // The coefficient row staged after the K rows: R(r_q - rho), the query's
 // rotation for this visit (R(r_q) when the keys are stored rotated to their
 // index).
-template <int D>
+template <int D, bool STREAM>
 __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, unsigned char* kbuf) {
     constexpr int RPI = 64 / (D / 8);            // rows per instruction
     const VisitSrc vs = visit_src(c, k);
@@ -740,17 +743,17 @@ __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, 
     for (int j = 0; j < 2 * (D / 32); ++j) {
         const int r = RPI * j + rl;
         const int col = 8 * (sl >> 3) + ((sl & 7) ^ k_swz(r));
-        dma16_stream(c.kp + (int64_t)(vs.tile * kTile + r) * D + 8 * col, kbuf + j * 1024);
+        dma16_policy<STREAM>(c.kp + (int64_t)(vs.tile * kTile + r) * D + 8 * col, kbuf + j * 1024);
     }
     dma_table_row<D>(c.table, c.rq - (c.prerot ? 0 : vs.rho), lane, kbuf + 2 * (D / 32) * 1024);
 }
 
-template <int D>
+template <int D, bool STREAM>
 __device__ __forceinline__ void dec_load_v(const DecodeCtx& c, int k, unsigned char* vbuf) {
     const VisitSrc vs = visit_src(c, k);
     const uint16_t* vb = c.vp + ((int64_t)(vs.tile * 4 + c.gq) * D + c.n) * 8;
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) dma16_stream(vb + (int64_t)nb * 16 * 8, vbuf + nb * 1024);
+    for (int nb = 0; nb < D / 16; ++nb) dma16_policy<STREAM>(vb + (int64_t)nb * 16 * 8, vbuf + nb * 1024);
 }
 
 // A visit's K part copied from LDS into registers: the query-rotation pairs
@@ -929,7 +932,7 @@ __device__ __forceinline__ uint64_t merge_partials(uint64_t a, uint64_t b) {
     return pack_partial(o, mx + __builtin_amdgcn_logf(sw));
 }
 
-template <int D, bool PREROT, bool PRE>
+template <int D, bool PREROT, bool PRE, bool STREAM>
 __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, StreamBatch st,
                                                       const uint16_t* __restrict__ q,
                                                       uint16_t* __restrict__ out, int n_split,
@@ -1044,14 +1047,14 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     // then K(k), V(k), K(k + 4), V(k + 4) of the wave's first two visits (those
     // that exist), and a wait for everything up to K(k)
     if (k + 4 < k1) {
-        dec_load_k<D>(c, k, lane, ka);
-        dec_load_v<D>(c, k, va);
-        dec_load_k<D>(c, k + 4, lane, kb);
-        dec_load_v<D>(c, k + 4, vb);
+        dec_load_k<D, STREAM>(c, k, lane, ka);
+        dec_load_v<D, STREAM>(c, k, va);
+        dec_load_k<D, STREAM>(c, k + 4, lane, kb);
+        dec_load_v<D, STREAM>(c, k + 4, vb);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV + B::nK + B::nV));
     } else if (k < k1) {
-        dec_load_k<D>(c, k, lane, ka);
-        dec_load_v<D>(c, k, va);
+        dec_load_k<D, STREAM>(c, k, lane, ka);
+        dec_load_v<D, STREAM>(c, k, va);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
     } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1107,13 +1110,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         if (k == k_tok) patch_k<D>(ka, t_tok, lane, ((const u32x4*)lds_tok)[lane & (D / 8 - 1)]);
         dec_read_k<D>(c, ka, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);                                 // copied out of ka
-        if (k + 8 < k1) dec_load_k<D>(c, k + 8, lane, ka);
+        if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, ka);
         bf16x8 pb = dec_scores<D, true>(c, k, rk, qraw, lds_rw, o, m, l);
         wait_v(k);
         if (k == k_tok) patch_v<D>(va, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(va, lane, rv);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_v<D>(c, k + 8, va);
+        if (k + 8 < k1) dec_load_v<D, STREAM>(c, k + 8, va);
         dec_pv<D>(rv, pb, o);
         k += 4;
         if (k >= k1) break;
@@ -1121,13 +1124,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         if (k == k_tok) patch_k<D>(kb, t_tok, lane, ((const u32x4*)lds_tok)[lane & (D / 8 - 1)]);
         dec_read_k<D>(c, kb, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_k<D>(c, k + 8, lane, kb);
+        if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, kb);
         pb = dec_scores<D, false>(c, k, rk, qraw, lds_rw, o, m, l);
         wait_v(k);
         if (k == k_tok) patch_v<D>(vb, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(vb, lane, rv);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_v<D>(c, k + 8, vb);
+        if (k + 8 < k1) dec_load_v<D, STREAM>(c, k + 8, vb);
         dec_pv<D>(rv, pb, o);
         k += 4;
     }
@@ -1813,8 +1816,11 @@ hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, 
     const int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, D == 128 ? n_cu : 2 * n_cu, 4);
     // three instances: the method, the method with a pinned prefix in the batch,
     // and the rebase-on-evict variant (which has no prefix)
-    auto kern = g.prerot ? decode_mfma<D, true, false>
-              : any_prefix(st) ? decode_mfma<D, false, true> : decode_mfma<D, false, false>;
+    // streaming loads when the launch's windows exceed the chip's L2 (8 x 4 MB)
+    const bool stream = (int64_t)st.nb * g.hkv * g.w_pad * D * 4 > (int64_t)32 << 20;
+    auto kern = g.prerot ? (stream ? decode_mfma<D, true, false, true> : decode_mfma<D, true, false, false>)
+              : any_prefix(st) ? (stream ? decode_mfma<D, false, true, true> : decode_mfma<D, false, true, false>)
+                               : (stream ? decode_mfma<D, false, false, true> : decode_mfma<D, false, false, false>);
     hipLaunchKernelGGL(kern, dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st, (const uint16_t*)q,
                        (uint16_t*)out, n_split, (const uint16_t*)k_new, (const uint16_t*)v_new);
     return hipGetLastError();
