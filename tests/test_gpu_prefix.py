@@ -254,3 +254,23 @@ def test_prefix_3b_shape():
             tw.chunk(0, 0, rand(rng, 4, 16, hq, d))
     say("worst err", tw.worst)
     tw.close()
+
+
+def test_prefix_streaming_launch():
+    """10 streams of the 3B-class shape (W = 4096): the launch's windows (42 MB)
+    exceed the L2, so decode takes the instance with streaming K/V loads, here
+    with a 64-token prefix; decode and fused decode against the oracle."""
+    say("prefix_streaming_launch")
+    rng = np.random.default_rng(26)
+    hq, hkv, d, w, nb = 16, 2, 128, 4096, 10
+    tw = Twin(1, nb, hq, hkv, d, w, 512, True, prefix_capacity=64)
+    tw.reset(0, [1000 * b + 3 for b in range(nb)], [(b * 613) % w for b in range(nb)])
+    tw.append_prefix(0, 0, rand(rng, nb, 64, hkv, d), rand(rng, nb, 64, hkv, d))
+    for _ in range(8):
+        tw.append(0, 0, rand(rng, nb, 512, hkv, d), rand(rng, nb, 512, hkv, d))
+    tw.decode(0, 0, rand(rng, nb, hq, d))
+    for _ in range(3):
+        tw.append_decode(0, 0, rand(rng, nb, 1, hkv, d), rand(rng, nb, 1, hkv, d), rand(rng, nb, hq, d))
+    say("worst err", tw.worst)
+    tw.close()
+

@@ -122,6 +122,27 @@ def test_rebase_fused_append_decode():
     tw.close()
 
 
+def test_rebase_streaming_launch():
+    """10 streams of the 3B-class shape (W = 4096, 42 MB of windows per launch):
+    decode takes the instance with streaming K/V loads; the stored keys after a
+    full window and evicting appends bit for bit, and attention within
+    tolerance."""
+    say("rebase streaming launch")
+    rng = np.random.default_rng(13)
+    hq, hkv, d, w, nb = 16, 2, 128, 4096, 10
+    tw = VariantTwin(nb, hq, hkv, d, w, 512, True, p0=[5 * b for b in range(nb)],
+                     s0=[(b * 977) % w for b in range(nb)])
+    for _ in range(8):
+        tw.append(_rand(rng, (nb, 512, hkv, d), True), _rand(rng, (nb, 512, hkv, d), True))
+    tw.attend(_rand(rng, (nb, 1, hq, d), True))
+    for _ in range(2):
+        tw.append(_rand(rng, (nb, 1, hkv, d), True), _rand(rng, (nb, 1, hkv, d), True))
+        tw.attend(_rand(rng, (nb, 1, hq, d), True))
+    tw.check_ring()
+    say("worst err", tw.worst)
+    tw.close()
+
+
 def test_drift_3b_stream():
     """Both cache modes on one 3B-shaped stream for three windows; errors
     against the exact re-based attention at checkpoints."""
