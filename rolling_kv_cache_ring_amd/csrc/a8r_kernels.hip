@@ -619,17 +619,7 @@ __device__ __forceinline__ VisitSrc visit_src(const DecodeCtx& c, int k) {
 }
 
 // (cos, sin) of the lane's 8*(D/64) pairs (dims 8*gq + 32*kk + e, kk < D/64)
-// of table row `row`.
-template <int D>
-__device__ __forceinline__ void load_coef(const float2* table, int row, int gq, float4 (&cf)[D / 64][4]) {
-    const float4* p = (const float4*)(table + (int64_t)row * (D / 2) + 8 * gq);
-#pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cf[kk][j] = p[16 * kk + j];   // pairs 32*kk + 2j, 2j + 1
-}
-
-// The same pairs read from a table row staged in LDS.
+// of a table row staged in LDS.
 template <int D>
 __device__ __forceinline__ void lds_coef(const unsigned char* row, int gq, float4 (&cf)[D / 64][4]) {
     const float4* p = (const float4*)row + 4 * gq;
@@ -1150,6 +1140,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
 
     // Across the block's 4 waves: each wave rescales its {l, O} to the block's
     // running max before writing them, so that the per-element merge is a sum.
+    // The first barrier also means every wave is done with its visit buffers,
+    // which red_o overlays.
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (n < G && gq == 0) red_ml[wave][n][0] = m;
