@@ -48,8 +48,8 @@ def parse():
                     choices=["qwen3b_batch64", "qwen3b_chunk8", "qwen3b_chunk12", "qwen3b_chunk16",
                              "qwen3b_single", "audio8_0p1b"])
     ap.add_argument("--path", default="fused", choices=["fused", "separate"],
-                    help="decode step per layer as one a8r_append_decode_attn call (fused) or as "
-                         "a8r_append_kv + a8r_decode_attn (separate)")
+                    help="step per layer as one a8r_append_decode_attn / a8r_append_chunk_attn call "
+                         "(fused) or as a8r_append_kv + a8r_decode_attn / a8r_chunk_attn (separate)")
     ap.add_argument("--cache-mode", default="rotate_on_read", choices=["rotate_on_read", "rebase_on_evict"],
                     help="rebase_on_evict runs the comparison variant (keys stored rotated and re-rotated at "
                          "every eviction); the fused call then runs as append + decode")
@@ -295,7 +295,7 @@ def main():
     h = cache.handle
     L = a8r.lib()
 
-    fused = c == 1 and args.path == "fused" and not rebase
+    fused = args.path == "fused" and not rebase
 
     def check(st):
         if st:
@@ -304,9 +304,13 @@ def main():
     def step(i):
         kp, vp, qp = k_ptrs[i % POOL], v_ptrs[i % POOL], q_ptrs[i % POOL]
         for layer in range(NL):
-            if fused:
+            if fused and c == 1:
                 check(L.a8r_append_decode_attn(h, layer, 0, B, kp[layer], vp[layer], qp[layer],
                                                o_ptrs[layer], None, None))
+                continue
+            if fused:
+                check(L.a8r_append_chunk_attn(h, layer, 0, B, c, kp[layer], vp[layer], qp[layer],
+                                              o_ptrs[layer], None, None))
                 continue
             check(L.a8r_append_kv(h, layer, 0, B, c, kp[layer], vp[layer], None, None))
             if c == 1:
@@ -339,10 +343,11 @@ def main():
     steps_per_s = 1000.0 / ms
 
     # average launch duration of the attention kernel.  Fused path: the timed
-    # region launches nothing else (one kernel per layer), so it is the region
-    # time over its launches.  Separate path: a second pass launches only the
-    # attention calls (they leave the cache unchanged) back to back on the same
-    # stream, bracketed by one event pair.
+    # region launches nothing else (one call per layer: the fused kernel, plus
+    # the split combine for a chunk), so it is the region time over its calls.
+    # Separate path: a second pass launches only the attention calls (they
+    # leave the cache unchanged) back to back on the same stream, bracketed by
+    # one event pair.
     if fused:
         n_launch = args.steps * NL
         attn_ms = ev0.elapsed_time(ev1) / n_launch
@@ -396,8 +401,9 @@ def main():
         "bytes_per_step": bytes_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("a8r_append_decode_attn (decode_mfma, fused append)" if fused else
-                       "a8r_decode_attn" if c == 1 else "a8r_chunk_attn"),
+            "kernel": ("a8r_append_decode_attn (decode_mfma, fused append)" if fused and c == 1 else
+                       "a8r_append_chunk_attn (chunk_pipe, fused append, + combine_kernel)" if fused else
+                       "a8r_decode_attn" if c == 1 else "a8r_chunk_attn (chunk_pipe + combine_kernel)"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -248,6 +248,20 @@ a8r_status a8r_append_decode_attn(a8r_cache* cache, int32_t layer, int32_t b0, i
                                   const void* v, const void* q, void* out, int32_t* slots_out,
                                   int64_t* evicted_out);
 
+/* The same for a chunk: exactly a8r_append_kv with n_new tokens followed by
+ * a8r_chunk_attn with n_new queries on the same streams, as one launch where
+ * the chunk kernel covers the shape (bfloat16, head_dim 64 or 128,
+ * 2 <= n_new, n_new * group <= 128, keys not stored rotated to their index;
+ * the block that owns a new token's 32-slot tile writes it before walking).
+ * n_new = 1 is a8r_append_decode_attn.  k, v: device
+ * [nb][n_new][n_kv_heads][head_dim]; q, out: device [nb][n_new][n_q_heads][head_dim];
+ * slots_out / evicted_out: host [nb][n_new] or NULL.  Source: as
+ * a8r_chunk_attn.  Errors: as a8r_append_kv and a8r_chunk_attn; nothing
+ * changes on error. */
+a8r_status a8r_append_chunk_attn(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb, int32_t n_new,
+                                 const void* k, const void* v, const void* q, void* out, int32_t* slots_out,
+                                 int64_t* evicted_out);
+
 /* Read the state of one (layer, stream) pair: next position P, live count L,
  * next slot S (host outputs, any may be NULL).  Synchronizes the stream and
  * checks the device-side copy against the host bookkeeping; a mismatch returns

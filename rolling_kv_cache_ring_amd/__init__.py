@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ENOMEM", 3: "EDEVICE", 4: "ESTATE", 5:
 
 EXPORTED = [
     "a8r_workspace_bytes", "a8r_cache_create", "a8r_cache_destroy", "a8r_set_stream", "a8r_reset",
-    "a8r_append_kv", "a8r_decode_attn", "a8r_chunk_attn", "a8r_append_decode_attn",
+    "a8r_append_kv", "a8r_decode_attn", "a8r_chunk_attn", "a8r_append_decode_attn", "a8r_append_chunk_attn",
     "a8r_get_state", "a8r_read_ring", "a8r_append_prefix", "a8r_export_prefix", "a8r_import_prefix", "a8r_clear_prefix",
     "a8r_prefix_length",
     "a8r_last_error", "a8r_ledger_create", "a8r_ledger_destroy", "a8r_ledger_reset",
@@ -97,6 +97,9 @@ def lib():
     L.a8r_append_decode_attn.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32p, _i64p]
     L.a8r_append_decode_attn.restype = st
+    L.a8r_append_chunk_attn.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32p, _i64p]
+    L.a8r_append_chunk_attn.restype = st
     L.a8r_append_prefix.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     _c_void_p, _c_void_p]
     L.a8r_append_prefix.restype = st
@@ -236,6 +239,19 @@ def append_decode_attn(handle: int, layer: int, b0: int, nb: int, k, v, q, out, 
     return None, None
 
 
+def append_chunk_attn(handle: int, layer: int, b0: int, nb: int, n_new: int, k, v, q, out, want_bookkeeping=True):
+    """a8r_append_kv (n_new tokens per stream) + a8r_chunk_attn in one launch."""
+    if want_bookkeeping:
+        slots = np.empty((nb, n_new), dtype=np.int32)
+        ev = np.empty((nb, n_new), dtype=np.int64)
+        _check(lib().a8r_append_chunk_attn(handle, layer, b0, nb, n_new, _ptr(k), _ptr(v), _ptr(q), _ptr(out),
+                                           slots.ctypes.data_as(_i32p), ev.ctypes.data_as(_i64p)))
+        return slots, ev
+    _check(lib().a8r_append_chunk_attn(handle, layer, b0, nb, n_new, _ptr(k), _ptr(v), _ptr(q), _ptr(out),
+                                       None, None))
+    return None, None
+
+
 def get_state(handle: int, layer: int, b: int) -> tuple[int, int, int]:
     p, n, s = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
     _check(lib().a8r_get_state(handle, layer, b, ctypes.byref(p), ctypes.byref(n), ctypes.byref(s)))
@@ -283,6 +299,9 @@ class Cache:
 
     def append_decode_attn(self, layer, b0, nb, k, v, q, out, want_bookkeeping=True):
         return append_decode_attn(self.handle, layer, b0, nb, k, v, q, out, want_bookkeeping)
+
+    def append_chunk_attn(self, layer, b0, nb, n_new, k, v, q, out, want_bookkeeping=True):
+        return append_chunk_attn(self.handle, layer, b0, nb, n_new, k, v, q, out, want_bookkeeping)
 
     def get_state(self, layer, b):
         return get_state(self.handle, layer, b)

@@ -493,6 +493,31 @@ a8r_status a8r_append_decode_attn(a8r_cache* c, int32_t layer, int32_t b0, int32
     return ok();
 }
 
+a8r_status a8r_append_chunk_attn(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_new,
+                                 const void* k, const void* v, const void* q, void* out, int32_t* slots_out,
+                                 int64_t* evicted_out) {
+    a8r_status st = check_live(c);
+    if (st != A8R_OK) return st;
+    if ((st = c->ledger.check_append(layer, b0, nb, n_new)) != A8R_OK) return st;
+    if (n_new > c->cfg.max_chunk) return fail(A8R_EINVAL, "n_new %d > max_chunk %d", n_new, c->cfg.max_chunk);
+    if (!k || !v) return fail(A8R_EINVAL, "k or v is NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(A8R_EINVAL, "k and v must be 16-byte aligned");
+    if ((st = check_attention(c, layer, b0, nb, n_new, n_new, q, out)) != A8R_OK) return st;
+    const size_t kvrow = (size_t)n_new * c->cfg.n_kv_heads * c->cfg.head_dim * c->geo.elem_bytes;
+    const size_t qrow = (size_t)n_new * c->cfg.n_q_heads * c->cfg.head_dim * c->geo.elem_bytes;
+    for (int32_t i0 = 0; i0 < nb; i0 += a8r::kBatch) {
+        a8r::StreamBatch sb;
+        fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
+        hipError_t e = a8r::launch_append_chunk(c->geo, layer, sb, n_new, (const uint8_t*)k + i0 * kvrow,
+                                                (const uint8_t*)v + i0 * kvrow, (const uint8_t*)q + i0 * qrow,
+                                                (uint8_t*)out + i0 * qrow,
+                                                c->cfg.kernel_policy == A8R_KERNELS_AUTO, c->n_cu, c->stream);
+        if (e != hipSuccess) return device_fail(c, e, "append+chunk kernel");
+    }
+    c->ledger.append(layer, b0, nb, n_new, slots_out, evicted_out);
+    return ok();
+}
+
 static a8r_status append_prefix(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_new, const void* k,
                                 const void* v, bool encode) {
     a8r_status st = check_live(c);

@@ -109,5 +109,10 @@ hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now
 hipError_t launch_append_decode(const Geometry& g, int layer, const StreamBatch& before,
                                 const void* k, const void* v, const void* q, void* out,
                                 bool allow_mfma, int n_cu, hipStream_t s);
+// n new tokens per stream appended and attended in one launch where the MFMA
+// chunk kernel runs with one row group (else append + attention).
+hipError_t launch_append_chunk(const Geometry& g, int layer, const StreamBatch& before, int n,
+                               const void* k, const void* v, const void* q, void* out,
+                               bool allow_mfma, int n_cu, hipStream_t s);
 
 }  // namespace a8r

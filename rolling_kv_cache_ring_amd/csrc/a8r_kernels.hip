@@ -1320,7 +1320,9 @@ struct PipeBuf {
 template <int D, int NW, int WG, bool PRE>
 __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer, StreamBatch st, int C,
                                                      const uint16_t* __restrict__ q,
-                                                     uint16_t* __restrict__ out, int n_split) {
+                                                     uint16_t* __restrict__ out, int n_split,
+                                                     const uint16_t* __restrict__ k_new,
+                                                     const uint16_t* __restrict__ v_new) {
     constexpr int KK = D / 32, NB = D / 16, HP = D / 64;
     constexpr int P = D / 16;                          // rotation pairs per lane (8 lanes per key)
     using PB = PipeBuf<D>;
@@ -1342,11 +1344,16 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     const int b = st.b0 + bi, G = g.group, W = g.window;
     const int rows = C * G;                            // rows of this block: row0 + 16 (wave + 4w) + n
 
+    // window after the (optional) append of the C new tokens: with k_new the
+    // state in the arguments is the state before it
+    const bool fused = k_new != nullptr;
+    const int s_prev = st.next_slot[bi];
+    const int L = fused ? min(st.length[bi] + C, W) : st.length[bi];
+    const int next_slot = fused ? wrap_slot(s_prev + C, W) : s_prev;
     DecodeCtx c;
-    const int L = st.length[bi];
     c.L = L;
     c.W = W;
-    c.oldest = st.next_slot[bi] - L < 0 ? st.next_slot[bi] - L + W : st.next_slot[bi] - L;
+    c.oldest = next_slot - L < 0 ? next_slot - L + W : next_slot - L;
     c.rq = L - C;                      // index of the chunk's first query
     c.n_tiles = g.w_pad / kTile;
     c.p0t = c.oldest / kTile;
@@ -1384,6 +1391,45 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     const int n_mine = k0 + wg < k1 ? (k1 - k0 - wg + WG - 1) / WG : 0;
     const int n_steps = (k1 - k0 + WG - 1) / WG;
     auto kvis = [&](int v) { return k0 + wg + WG * v; };
+
+    // Fused append (one row group): the new tokens of this (stream, KV head)
+    // whose tiles are among this block's visits are written into their ring
+    // slots first, tile-phase encoded as append_kernel writes them, and the
+    // block waits for the stores before any of its loads.  No other block reads
+    // those tiles in this call.
+    if (fused) {
+        auto visit_of = [&](int slot) {
+            const int v = slot / kTile - c.p0t;
+            return v < 0 ? v + c.n_tiles : v;
+        };
+        bool mine = false;                             // block-uniform
+        for (int j = 0; j < C; ++j) {
+            const int v = visit_of(wrap_slot(s_prev + j, W));
+            mine = mine || (v >= k0 && v < k1);
+        }
+        if (mine) {
+            constexpr int halfc = D / 16;              // chunk pairs of a bf16 row
+            for (int t = tid; t < C * halfc; t += 256 * WG) {
+                const int j = t / halfc, cc = t - j * halfc;
+                const int slot = wrap_slot(s_prev + j, W);
+                const int v = visit_of(slot);
+                if (v >= k0 && v < k1) {
+                    const int64_t src = (((int64_t)bi * C + j) * g.hkv + kh) * D * 2;
+                    write_token_pair<2>(g, pair, slot, cc, true, (const uint8_t*)k_new + src,
+                                        (const uint8_t*)v_new + src);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);             // the tokens are in the L2 ...
+            __syncthreads();                           // ... before any wave loads a tile
+        }
+        if (kh == 0 && split == 0 && tid == 0) {      // record of the new state
+            DevState ns;
+            ns.next_pos = st.next_pos[bi] + C;
+            ns.length = L;
+            ns.next_slot = next_slot;
+            g.state[(int64_t)layer * g.n_streams + b] = ns;
+        }
+    }
 
     // this wave's quarter of local visit v's K part (rows + a quarter of the
     // R(rho) row, |rho| for the first visit) and of its V part
@@ -1820,13 +1866,14 @@ hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, 
 
 template <int D, int NW>
 hipError_t run_chunk_pipe(const Geometry& g, int layer, const StreamBatch& st, int n_q, const void* q, void* out,
-                          int n_cu, hipStream_t s) {
+                          int n_cu, hipStream_t s, const void* k_new = nullptr, const void* v_new = nullptr) {
     const int n_rg = (n_q * g.group + 127) / 128;      // row groups of up to 128 query rows
     const int n_split = pick_splits(st.nb * g.hkv * n_rg, g.w_pad / kTile, n_cu, 4);
     // two wave groups per block: two waves per SIMD
     auto kern = any_prefix(st) ? chunk_pipe<D, NW, 2, true> : chunk_pipe<D, NW, 2, false>;
     hipLaunchKernelGGL(kern, dim3(n_split * n_rg, g.hkv, st.nb), dim3(512), 0, s, g, layer, st, n_q,
-                       (const uint16_t*)q, (uint16_t*)out, n_split);
+                       (const uint16_t*)q, (uint16_t*)out, n_split, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split == 1) return e;
     // the splits' partials are merged by a second, chip-wide kernel
@@ -1932,6 +1979,31 @@ hipError_t launch_append_decode(const Geometry& g, int layer, const StreamBatch&
         now.next_slot[i] = now.next_slot[i] + 1 == g.window ? 0 : now.next_slot[i] + 1;
     }
     return launch_attention(g, layer, now, 1, q, out, allow_mfma, n_cu, s);
+}
+
+hipError_t launch_append_chunk(const Geometry& g, int layer, const StreamBatch& before, int n, const void* k,
+                               const void* v, const void* q, void* out, bool allow_mfma, int n_cu, hipStream_t s) {
+    if (n == 1) return launch_append_decode(g, layer, before, k, v, q, out, allow_mfma, n_cu, s);
+    // one launch where the chunk kernel runs with a single row group (a second
+    // row group would read the new tokens' tiles while the first writes them)
+    if (allow_mfma && mfma_chunk_ok(g, n) && !g.prerot && n * g.group <= 128) {
+        const bool one = n * g.group <= 64;
+        if (g.d == 128)
+            return one ? run_chunk_pipe<128, 1>(g, layer, before, n, q, out, n_cu, s, k, v)
+                       : run_chunk_pipe<128, 2>(g, layer, before, n, q, out, n_cu, s, k, v);
+        return one ? run_chunk_pipe<64, 1>(g, layer, before, n, q, out, n_cu, s, k, v)
+                   : run_chunk_pipe<64, 2>(g, layer, before, n, q, out, n_cu, s, k, v);
+    }
+    hipError_t e = launch_append(g, layer, before, n, k, v, s);
+    if (e == hipSuccess && g.prerot) e = launch_rebase(g, layer, before, n, s);
+    if (e != hipSuccess) return e;
+    StreamBatch now = before;
+    for (int i = 0; i < now.nb; ++i) {
+        now.next_pos[i] += n;
+        now.length[i] = min(now.length[i] + n, g.window);
+        now.next_slot[i] = (now.next_slot[i] + n) % g.window;
+    }
+    return launch_attention(g, layer, now, n, q, out, allow_mfma, n_cu, s);
 }
 
 }  // namespace a8r

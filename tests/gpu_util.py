@@ -131,6 +131,21 @@ class Twin:
             self._cmp(got, exp, ("append_decode", layer, b0))
         return got
 
+    def append_chunk(self, layer, b0, k, v, q, check=True):
+        """a8r_append_chunk_attn: k, v [nb, n, Hkv, D], q [nb, n, Hq, D]."""
+        nb, n = q.shape[:2]
+        out = empty_out((nb, n, self.hq, self.d), self.bf16)
+        slots, ev = self.gpu.append_chunk_attn(layer, b0, nb, n, to_device(k, self.bf16), to_device(v, self.bf16),
+                                               to_device(q, self.bf16), out)
+        s_ref, e_ref = self.ora.append(layer, b0, k, v)
+        assert np.array_equal(slots, np.array(s_ref, dtype=np.int32)), (slots, s_ref)
+        assert np.array_equal(ev, np.array(e_ref, dtype=np.int64)), (ev, e_ref)
+        got = to_host_f64(out, self.bf16)
+        if check:
+            exp = self.ora.chunk(layer, b0, q)
+            self._cmp(got, exp, ("append_chunk", layer, b0))
+        return got
+
     def chunk(self, layer, b0, q, check=True):
         nb, n = q.shape[:2]
         out = empty_out((nb, n, self.hq, self.d), self.bf16)

@@ -86,6 +86,41 @@ def test_fused_append_decode_wraps(window, hq, hkv, d, bf16, portable):
 
 
 @pytest.mark.parametrize("portable", [False, True])
+@pytest.mark.parametrize("window,chunk,hq,hkv,d,bf16,nb", [
+    (64, 8, 16, 2, 128, True, 3), (37, 5, 8, 8, 64, True, 2), (45, 16, 16, 2, 128, True, 2),
+    (50, 3, 4, 2, 64, False, 2),                          # float32: the two-launch path
+    (64, 12, 32, 2, 128, True, 2),                        # 192 query rows: the two-launch path
+    (2048, 8, 16, 2, 128, True, 2), (1000, 6, 8, 1, 64, True, 3),   # many key splits
+])
+def test_fused_append_chunk(window, chunk, hq, hkv, d, bf16, nb, portable):
+    """a8r_append_chunk_attn equals append + chunk through fills and wraps (new
+    tokens crossing tile and split boundaries, sizes 1 and odd), mixed with
+    separate appends and chunks on the same cache."""
+    say("fused_append_chunk", window, chunk, hq, hkv, d, bf16, nb, portable)
+    rng = np.random.default_rng(window * 3 + chunk)
+    tw = Twin(2, nb, hq, hkv, d, window, chunk, bf16, portable)
+    tw.reset(0, [2**24 - 3 * window + i for i in range(nb)], [int(rng.integers(window)) for _ in range(nb)])
+    steps = min(3 * window // chunk + 5, 40) if window > 512 else 3 * window // chunk + 5
+    for t in range(steps):
+        layer = t % 2
+        n = chunk if t % 4 else (1 if t % 8 == 0 else max(2, chunk - 3))
+        k = rand(rng, nb, n, hkv, d, bf16=bf16)
+        v = rand(rng, nb, n, hkv, d, bf16=bf16)
+        q = rand(rng, nb, n, hq, d, bf16=bf16)
+        if t % 7 == 6:
+            tw.append(layer, 0, k, v)
+            tw.chunk(layer, 0, q)
+        else:
+            tw.append_chunk(layer, 0, k, v, q)
+    for layer in range(2):
+        for b in range(nb):
+            tw.check_state(layer, b)
+            tw.check_ring(layer, b)
+    say("worst err", tw.worst)
+    tw.close()
+
+
+@pytest.mark.parametrize("portable", [False, True])
 @pytest.mark.parametrize("window,chunk,hq,hkv,d,bf16", [
     (64, 8, 16, 2, 128, True), (37, 5, 8, 8, 64, True), (16, 16, 16, 2, 128, True),
     (50, 3, 4, 2, 64, False), (128, 8, 16, 2, 128, True),

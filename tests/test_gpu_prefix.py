@@ -95,8 +95,11 @@ def test_prefix_chunk(window, chunk, hq, hkv, d, prefixes, portable):
             tw.append_prefix(0, b, rand(rng, 1, f, hkv, d), rand(rng, 1, f, hkv, d))
     for t in range(3 * window // chunk + 3):
         n = chunk if t % 3 else max(1, chunk // 2)
-        tw.append(0, 0, rand(rng, 2, n, hkv, d), rand(rng, 2, n, hkv, d))
-        q = rand(rng, 2, n, hq, d)
+        k, v, q = rand(rng, 2, n, hkv, d), rand(rng, 2, n, hkv, d), rand(rng, 2, n, hq, d)
+        if t % 2:                                   # one launch: append + attention
+            tw.append_chunk(0, 0, k, v, q)
+            continue
+        tw.append(0, 0, k, v)
         if n == 1:
             tw.decode(0, 0, q[:, 0])
         else:

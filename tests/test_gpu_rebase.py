@@ -55,12 +55,18 @@ class VariantTwin:
         tol = TOL_BF16 if self.bf16 else TOL_F32
         if fused_kv is not None:
             k, v = fused_kv
-            out = empty_out((b_n, self.hq, self.d), self.bf16)
-            self.gpu.append_decode_attn(0, 0, b_n, to_device(k, self.bf16), to_device(v, self.bf16),
-                                        to_device(q[:, 0], self.bf16), out)
+            if c == 1:
+                out = empty_out((b_n, self.hq, self.d), self.bf16)
+                self.gpu.append_decode_attn(0, 0, b_n, to_device(k, self.bf16), to_device(v, self.bf16),
+                                            to_device(q[:, 0], self.bf16), out)
+                got = to_host_f64(out, self.bf16)[:, None]
+            else:
+                out = empty_out((b_n, c, self.hq, self.d), self.bf16)
+                self.gpu.append_chunk_attn(0, 0, b_n, c, to_device(k, self.bf16), to_device(v, self.bf16),
+                                           to_device(q, self.bf16), out)
+                got = to_host_f64(out, self.bf16)
             for b in range(b_n):
                 self.ora[b].append(k[b], v[b])
-            got = to_host_f64(out, self.bf16)[:, None]
         elif c == 1:
             out = empty_out((b_n, self.hq, self.d), self.bf16)
             self.gpu.decode_attn(0, 0, b_n, to_device(q[:, 0], self.bf16), out)
@@ -118,6 +124,20 @@ def test_rebase_fused_append_decode():
     for t in range(2 * w + 9):
         k, v = _rand(rng, (3, 1, hkv, d), True), _rand(rng, (3, 1, hkv, d), True)
         tw.attend(_rand(rng, (3, 1, hq, d), True), fused_kv=(k, v))
+    tw.check_ring()
+    tw.close()
+
+
+def test_rebase_fused_append_chunk():
+    """In this mode a8r_append_chunk_attn runs as append + re-rotation + chunk."""
+    say("rebase fused append+chunk")
+    rng = np.random.default_rng(12)
+    hq, hkv, d, w = 16, 2, 128, 80
+    tw = VariantTwin(2, hq, hkv, d, w, 8, True, p0=[3, 2**24 - 5], s0=[0, 17])
+    for t in range(3 * w // 6 + 4):
+        n = 8 if t % 3 else 3
+        k, v = _rand(rng, (2, n, hkv, d), True), _rand(rng, (2, n, hkv, d), True)
+        tw.attend(_rand(rng, (2, n, hq, d), True), fused_kv=(k, v))
     tw.check_ring()
     tw.close()
 
