@@ -192,6 +192,11 @@ def test_errors_leave_state_unchanged():
         (lambda: c.decode_attn(0, 0, 2, 0, out), a8r.A8R_EINVAL),         # null q
         (lambda: c.reset(0, [-5]), a8r.A8R_EINVAL),
         (lambda: c.reset(1, [5], [64]), a8r.A8R_EINVAL),
+        (lambda: c.append_chunk_attn(0, 0, 2, 9, k, k, q, out), a8r.A8R_EINVAL),      # n_new > max_chunk
+        (lambda: c.append_chunk_attn(0, 1, 2, 4, k, k, q, out), a8r.A8R_EINVAL),      # streams out of range
+        (lambda: c.append_chunk_attn(0, 0, 2, 4, k, k, 0, out), a8r.A8R_EINVAL),      # null q
+        (lambda: c.append_chunk_attn(0, 0, 2, 4, k.data_ptr() + 2, k, q, out), a8r.A8R_EINVAL),
+        (lambda: c.append_decode_attn(0, 0, 2, k, k, q.data_ptr() + 2, out), a8r.A8R_EINVAL),
     ]
     for call, status in bad:
         with pytest.raises(a8r.A8RError) as e:
