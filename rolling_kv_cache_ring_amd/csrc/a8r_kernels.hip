@@ -62,6 +62,28 @@ constexpr float kNegBig = -1.0e30f;   // running-max seed: exp2(x - kNegBig) nev
 // and results below 2^-126 flush to 0, which is harmless for softmax weights.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max and sum over the lanes l, l^16, l^32, l^48 (the four lanes holding one
+// MFMA output column) with gfx950's lane-swap instructions: each swap returns
+// {x[l], x[l^16]} (resp. l^32) in some order, in VALU, without the LDS round
+// trip of a bpermute.  Both operations are commutative, so every lane of the
+// group gets the same bits.
+__device__ __forceinline__ float max_rows4(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned w = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_rows4(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned w = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -842,8 +864,7 @@ __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const De
     float mx = s[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_rows4(mx);
     // lazy rescale: keep the running max unless a score exceeds it by 2^8; the
     // branch is taken by the whole wave when any column needs it (the others
     // multiply by exactly 1)
@@ -1142,8 +1163,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     // running max before writing them, so that the per-element merge is a sum.
     // The first barrier also means every wave is done with its visit buffers,
     // which red_o overlays.
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = sum_rows4(l);
     if (n < G && gq == 0) red_ml[wave][n][0] = m;
     __syncthreads();
     {
@@ -1709,8 +1729,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
                 float mx = s8[0];
 #pragma unroll
                 for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s8[e]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = max_rows4(mx);
                 const bool grow = mx > m[w] + 8.f;       // lazy rescale, wave-uniform branch
                 if (__any(grow)) {
                     const float mn = grow ? mx : m[w];
@@ -1750,8 +1769,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     // column n) in o[w][nb][j]
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        l[w] += __shfl_xor(l[w], 16);
-        l[w] += __shfl_xor(l[w], 32);
+        l[w] = sum_rows4(l[w]);
     }
     if constexpr (WG == 2) {
         // group 1 hands its (m, l, O) of every row to group 0 through LDS
