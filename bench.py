@@ -234,7 +234,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
-              "(streams shard across GPUs with no exchange; see DESIGN.md). Run with --gpus 1.",
+              "(streams shard across GPUs with no exchange). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

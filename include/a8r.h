@@ -63,7 +63,7 @@ typedef enum a8r_status {
     A8R_ENOMEM = 2,        /* device allocation failed, or workspace too small */
     A8R_EDEVICE = 3,       /* a HIP call failed; the cache is now poisoned */
     A8R_ESTATE = 4,        /* call not valid in the current state (empty window, poisoned cache) */
-    A8R_EUNSUPPORTED = 5   /* valid request this build does not implement */
+    A8R_EUNSUPPORTED = 5   /* valid request this library does not implement */
 } a8r_status;
 
 typedef enum a8r_dtype { A8R_F32 = 0, A8R_BF16 = 1 } a8r_dtype;
