@@ -1412,45 +1412,6 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     const int n_steps = (k1 - k0 + WG - 1) / WG;
     auto kvis = [&](int v) { return k0 + wg + WG * v; };
 
-    // Fused append (one row group): the new tokens of this (stream, KV head)
-    // whose tiles are among this block's visits are written into their ring
-    // slots first, tile-phase encoded as append_kernel writes them, and the
-    // block waits for the stores before any of its loads.  No other block reads
-    // those tiles in this call.
-    if (fused) {
-        auto visit_of = [&](int slot) {
-            const int v = slot / kTile - c.p0t;
-            return v < 0 ? v + c.n_tiles : v;
-        };
-        bool mine = false;                             // block-uniform
-        for (int j = 0; j < C; ++j) {
-            const int v = visit_of(wrap_slot(s_prev + j, W));
-            mine = mine || (v >= k0 && v < k1);
-        }
-        if (mine) {
-            constexpr int halfc = D / 16;              // chunk pairs of a bf16 row
-            for (int t = tid; t < C * halfc; t += 256 * WG) {
-                const int j = t / halfc, cc = t - j * halfc;
-                const int slot = wrap_slot(s_prev + j, W);
-                const int v = visit_of(slot);
-                if (v >= k0 && v < k1) {
-                    const int64_t src = (((int64_t)bi * C + j) * g.hkv + kh) * D * 2;
-                    write_token_pair<2>(g, pair, slot, cc, true, (const uint8_t*)k_new + src,
-                                        (const uint8_t*)v_new + src);
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0);             // the tokens are in the L2 ...
-            __syncthreads();                           // ... before any wave loads a tile
-        }
-        if (kh == 0 && split == 0 && tid == 0) {      // record of the new state
-            DevState ns;
-            ns.next_pos = st.next_pos[bi] + C;
-            ns.length = L;
-            ns.next_slot = next_slot;
-            g.state[(int64_t)layer * g.n_streams + b] = ns;
-        }
-    }
-
     // this wave's quarter of local visit v's K part (rows + a quarter of the
     // R(rho) row, |rho| for the first visit) and of its V part
     // (a v past the group's visits loads the pair's first tile instead, which
@@ -1503,6 +1464,46 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         off = off < qcb ? off : qcb - 16;
         dma16((const unsigned char*)(g.table + (int64_t)c.rq * (D / 2)) + off, lds_qc + wave_b * 1024);
     }
+    // Fused append (one row group): the new tokens of this (stream, KV head)
+    // whose tiles are among this block's visits are written into their ring
+    // slots, tile-phase encoded as append_kernel writes them, and the block
+    // waits for the stores (and the query and table loads above, issued first
+    // so that their latency overlaps) before its first K/V load.  No other
+    // block reads those tiles in this call.
+    if (fused) {
+        auto visit_of = [&](int slot) {
+            const int v = slot / kTile - c.p0t;
+            return v < 0 ? v + c.n_tiles : v;
+        };
+        bool mine = false;                             // block-uniform
+        for (int j = 0; j < C; ++j) {
+            const int v = visit_of(wrap_slot(s_prev + j, W));
+            mine = mine || (v >= k0 && v < k1);
+        }
+        if (mine) {
+            constexpr int halfc = D / 16;              // chunk pairs of a bf16 row
+            for (int t = tid; t < C * halfc; t += 256 * WG) {
+                const int j = t / halfc, cc = t - j * halfc;
+                const int slot = wrap_slot(s_prev + j, W);
+                const int v = visit_of(slot);
+                if (v >= k0 && v < k1) {
+                    const int64_t src = (((int64_t)bi * C + j) * g.hkv + kh) * D * 2;
+                    write_token_pair<2>(g, pair, slot, cc, true, (const uint8_t*)k_new + src,
+                                        (const uint8_t*)v_new + src);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);             // the tokens are in the L2 ...
+            __syncthreads();                           // ... before any wave loads a tile
+        }
+        if (kh == 0 && split == 0 && tid == 0) {      // record of the new state
+            DevState ns;
+            ns.next_pos = st.next_pos[bi] + C;
+            ns.length = L;
+            ns.next_slot = next_slot;
+            g.state[(int64_t)layer * g.n_streams + b] = ns;
+        }
+    }
+
     issue_k(0, ring_k);
     issue_k(1, ring_k + PB::kKC);
     issue_v(0, ring_v);
