@@ -163,9 +163,21 @@ def test_ragged_streams_and_reset_midstream(portable):
     tw.decode(0, 0, rand(rng, 5, hq, d))
     tw.chunk(0, 1, rand(rng, 2, 3, hq, d))
     tw.decode(1, 1, rand(rng, 2, hq, d))
+    # fused calls over the ragged batch: an empty window filling up (layer 1,
+    # streams 0, 3, 4), partly filled and full windows in one launch
+    for t in range(4):
+        n = 4 if t % 2 else 1
+        k, v = rand(rng, 5, n, hkv, d), rand(rng, 5, n, hkv, d)
+        if n == 1:
+            tw.append_decode(1, 0, k, v, rand(rng, 5, hq, d))
+            tw.append_decode(0, 0, k, v, rand(rng, 5, hq, d))
+        else:
+            tw.append_chunk(1, 0, k, v, rand(rng, 5, n, hq, d))
+            tw.append_chunk(0, 0, k, v, rand(rng, 5, n, hq, d))
     for b in range(5):
         tw.check_state(0, b)
         tw.check_state(1, b)
+        tw.check_ring(0, b)
     tw.close()
 
 
