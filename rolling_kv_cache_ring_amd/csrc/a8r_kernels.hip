@@ -1832,8 +1832,11 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     }
 }
 
+// Key splits per pair: as many as keep the launch within target_blocks (the
+// blocks resident at once; rounding up would leave a second, mostly idle wave
+// of blocks), at most one per min_tiles_per_split tiles and kMaxSplits.
 int pick_splits(int pairs, int tiles, int target_blocks, int min_tiles_per_split) {
-    int sp = (target_blocks + pairs - 1) / pairs;
+    int sp = target_blocks / pairs;
     int cap = tiles / min_tiles_per_split;
     if (cap < 1) cap = 1;
     if (sp > cap) sp = cap;
@@ -1869,8 +1872,10 @@ hipError_t run_portable(const Geometry& g, int layer, const StreamBatch& st, int
 template <int D>
 hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, const void* q, void* out,
                            int n_cu, const void* k_new, const void* v_new, hipStream_t s) {
-    // one resident block per CU for D = 128 (one wave per SIMD), two for D = 64
-    const int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, D == 128 ? n_cu : 2 * n_cu, 4);
+    // one resident block per CU for D = 128 (one wave per SIMD), two for D = 64;
+    // at most 8 splits (a merge tree of 3 levels): for small batches a fourth
+    // level's exchange latency costs more than the shorter walks save
+    const int n_split = min(pick_splits(st.nb * g.hkv, g.w_pad / kTile, D == 128 ? n_cu : 2 * n_cu, 4), 8);
     // three instances: the method, the method with a pinned prefix in the batch,
     // and the rebase-on-evict variant (which has no prefix)
     // streaming loads when the launch's windows exceed the chip's L2 (8 x 4 MB)

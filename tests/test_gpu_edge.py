@@ -243,8 +243,8 @@ def test_bitwise_deterministic(portable, streams, window):
 
 @pytest.mark.parametrize("window", [400, 700, 950, 1600])
 def test_decode_merge_tree_split_counts(window):
-    """One stream (two KV heads): the window is split 3, 5, 7 and 12 ways (about a
-    quarter of its 32-slot tiles, up to 16), so the merge tree has unpaired
+    """One stream (two KV heads): the window is split 3, 5, 7 and 8 ways (about a
+    quarter of its 32-slot tiles, up to 8), so the merge tree has unpaired
     nodes that pass up; parity through fills and a wrap, and identical bits on
     repeated calls."""
     say("decode_merge_tree", window)
