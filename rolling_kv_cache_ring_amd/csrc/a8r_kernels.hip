@@ -1873,9 +1873,11 @@ template <int D>
 hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, const void* q, void* out,
                            int n_cu, const void* k_new, const void* v_new, hipStream_t s) {
     // one resident block per CU for D = 128 (one wave per SIMD), two for D = 64;
-    // at most 8 splits (a merge tree of 3 levels): for small batches a fourth
-    // level's exchange latency costs more than the shorter walks save
-    const int n_split = min(pick_splits(st.nb * g.hkv, g.w_pad / kTile, D == 128 ? n_cu : 2 * n_cu, 4), 8);
+    // at most 8 splits, rounded down to a power of two: each level of the merge
+    // tree adds an exchange latency that costs more than the shorter walks save
+    // (5 splits take the 3 levels of 8, 4 take 2)
+    int n_split = min(pick_splits(st.nb * g.hkv, g.w_pad / kTile, D == 128 ? n_cu : 2 * n_cu, 4), 8);
+    n_split = n_split >= 8 ? 8 : n_split >= 4 ? 4 : n_split >= 2 ? 2 : 1;
     // three instances: the method, the method with a pinned prefix in the batch,
     // and the rebase-on-evict variant (which has no prefix)
     // streaming loads when the launch's windows exceed the chip's L2 (8 x 4 MB)

@@ -243,10 +243,10 @@ def test_bitwise_deterministic(portable, streams, window):
 
 @pytest.mark.parametrize("window", [400, 700, 950, 1600])
 def test_decode_merge_tree_split_counts(window):
-    """One stream (two KV heads): the window is split 3, 5, 7 and 8 ways (about a
-    quarter of its 32-slot tiles, up to 8), so the merge tree has unpaired
-    nodes that pass up; parity through fills and a wrap, and identical bits on
-    repeated calls."""
+    """One stream (two KV heads): the window is split 2, 4, 4 and 8 ways (a
+    quarter of its 32-slot tiles rounded down to a power of two, up to 8): merge
+    trees of 1 to 3 levels; parity through fills and a wrap, and identical bits
+    on repeated calls."""
     say("decode_merge_tree", window)
     rng = np.random.default_rng(window)
     tw = Twin(1, 1, 16, 2, 128, window, 1, True)
