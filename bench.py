@@ -79,86 +79,148 @@ def copy_probe(torch):
     del src, dst
 
 
+# kernels of one attention call (what roofline.achieved times): the fused or
+# separate attention kernel and, for split chunks, the split merge
+CALL_KERNELS = ("decode_mfma", "chunk_pipe", "combine_kernel", "attn_portable")
+
+
+def short_name(name):
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def kernel_family(name):
+    for k in CALL_KERNELS:
+        if k in name:
+            return k
+    return None
+
+
 def summarize(args):
-    """Reads rocprofv3 CSVs (kernel_stats / counter_collection) under a directory
-    and prints a markdown summary; for counter runs also updates
-    profiles/pmc_traffic.json with the calibrated HBM bytes per attention launch."""
+    """Reads rocprofv3 CSVs under a directory and prints a markdown summary.
+
+    Kernel traces (kernel_trace.csv): per-kernel durations over the steady
+    state, i.e. after the first warmup x layers dispatches of each attention
+    kernel (the benchmark's untimed warm-up calls); kernel_stats.csv rows are
+    listed too (all dispatches).  Counters (counter_collection.csv): per-kernel
+    steady-state averages of every counter; FETCH_SIZE / WRITE_SIZE are scaled
+    by what the same counter reads for the plain 1 GiB copies of --copy-probe,
+    summed over the kernels of one attention call, and recorded in
+    profiles/pmc_traffic.json with the kernel source's hash."""
     import csv
     import glob
     from collections import defaultdict
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    skip = args.warmup * wl.n_layers
     d = args.summarize
     lines = [f"command: `{args.summary_command}`", ""]
-    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    for f in stats:
-        rows = list(csv.DictReader(open(f)))
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        per = defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            per[short_name(r["Kernel_Name"])].append(
+                (int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+        lines.append(f"Steady state: the first {skip} dispatches of each attention kernel (warm-up) are left out.")
+        lines.append("")
+        lines.append("| kernel | dispatches | steady | avg us | median us | min us | max us |")
+        lines.append("|---|---|---|---|---|---|---|")
+        call_us = 0.0
+        for name, ds in sorted(per.items(), key=lambda kv: -sum(x[1] for x in kv[1])):
+            ds.sort()
+            steady = ds[skip:] if kernel_family(name) else ds
+            if not steady:
+                continue
+            us = np.array([x[1] for x in steady])
+            if kernel_family(name):
+                call_us += float(us.mean())
+            lines.append(f"| `{name[:70]}` | {len(ds)} | {len(steady)} | {us.mean():.2f} | {np.median(us):.2f} | "
+                         f"{us.min():.2f} | {us.max():.2f} |")
+        lines.append(f"\nattention call (sum of its kernels' steady-state averages): {call_us:.2f} us")
+    for f in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+        lines.append("")
+        lines.append("kernel_stats.csv (all dispatches, warm-up included):")
+        lines.append("")
         lines.append("| kernel | calls | avg us | min us | max us | share |")
         lines.append("|---|---|---|---|---|---|")
-        for r in rows:
-            name = r["Name"]
-            short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-            lines.append(f"| `{short[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        for r in csv.DictReader(open(f)):
+            lines.append(f"| `{short_name(r['Name'])[:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                          f"{float(r['Percentage']):.1f}% |")
     cc = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if cc:
-        per = defaultdict(lambda: defaultdict(float))
-        calls = defaultdict(set)
         rows_all = []
         for f in cc:
             rows_all += list(csv.DictReader(open(f)))
-        is_attn = lambda n: "decode_mfma" in n or "chunk_mfma" in n or "chunk_tiled" in n or "chunk_pipe" in n
-        last_attn = max([int(r["Dispatch_Id"]) for r in rows_all if is_attn(r["Kernel_Name"])] + [0])
+        # per kernel family: dispatch id -> {counter: value}
+        disp = defaultdict(lambda: defaultdict(lambda: defaultdict(float)))
         for r in rows_all:
-            name = r["Kernel_Name"]
-            if is_attn(name):
-                key = "attention"
-            elif "copy" in name.lower() and int(r["Dispatch_Id"]) > last_attn:
-                key = "copy"        # the calibration copies run after the last attention launch
-            else:
+            fam = kernel_family(r["Kernel_Name"])
+            if fam is None and "copy" in r["Kernel_Name"].lower():
+                fam = "copy"
+            if fam is None:
                 continue
-            per[key][r["Counter_Name"]] += float(r["Counter_Value"])
-            calls[key].add(r["Dispatch_Id"])
-        lines.append("| kernel | dispatches | counter | KiB per dispatch |")
-        lines.append("|---|---|---|---|")
+            disp[fam][int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        last_attn = max([i for fam, dd in disp.items() if fam != "copy" for i in dd] + [0])
         avg = {}
-        for key, cnt in per.items():
-            for cname, v in cnt.items():
-                a = v / max(1, len(calls[key]))
-                avg[(key, cname)] = a
-                lines.append(f"| {key} | {len(calls[key])} | {cname} | {a:.1f} |")
-        rec_path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+        lines.append("")
+        lines.append(f"Counters per dispatch, steady state (the first {skip} dispatches of each attention kernel "
+                     f"left out):")
+        lines.append("")
+        lines.append("| kernel | dispatches averaged | counter | value per dispatch |")
+        lines.append("|---|---|---|---|")
+        for fam in sorted(disp):
+            ids = sorted(disp[fam])
+            if fam == "copy":
+                ids = [i for i in ids if i > last_attn]     # the calibration copies come last
+            else:
+                ids = ids[skip:]
+            if not ids:
+                continue
+            names = sorted({c for i in ids for c in disp[fam][i]})
+            for cname in names:
+                v = float(np.mean([disp[fam][i].get(cname, 0.0) for i in ids]))
+                avg[(fam, cname)] = v
+                unit = " KiB" if cname in ("FETCH_SIZE", "WRITE_SIZE") else ""
+                lines.append(f"| {fam} | {len(ids)} | {cname} | {v:.4g}{unit} |")
+        rec_path = PMC_FILE
         try:
             rec = json.load(open(rec_path))
         except (OSError, ValueError):
             rec = {}
-        wl = args.workload + (f"+prefix{args.prefix}" if args.prefix else "")
-        entry = rec.get(wl, {})
+        key = args.workload + (f"+prefix{args.prefix}" if args.prefix else "")
+        entry = rec.get(key, {})
         if entry.get("kernel_sha256_16") != kernel_hash():
             entry = {}      # counters taken on an older kernel source no longer apply
-        for cname, copy_bytes in (("FETCH_SIZE", COPY_PROBE_BYTES), ("WRITE_SIZE", COPY_PROBE_BYTES)):
-            if ("copy", cname) in avg and ("attention", cname) in avg:
-                factor = copy_bytes / (avg[("copy", cname)] * 1024)
-                entry[cname.lower() + "_factor"] = factor
-                entry[cname.lower() + "_bytes"] = avg[("attention", cname)] * 1024 * factor
-                lines.append(f"\n{cname}: copy probe counts {avg[('copy', cname)]:.0f} KiB for "
-                             f"{copy_bytes / 1024:.0f} KiB moved -> scale factor {factor:.4f}; attention kernel "
-                             f"{avg[('attention', cname)] * 1024 * factor / 1e6:.2f} MB per launch")
-        entry["kernel_sha256_16"] = kernel_hash()
-        entry["path"] = args.path
-        if "fetch_size_bytes" in entry and "write_size_bytes" in entry:
-            entry["bytes_per_launch"] = round(entry["fetch_size_bytes"] + entry["write_size_bytes"])
-            lines.append(f"\nrecorded {rec_path}: {entry['bytes_per_launch'] / 1e6:.2f} MB per launch")
-        rec[wl] = entry
-        os.makedirs(os.path.dirname(rec_path), exist_ok=True)
-        json.dump(rec, open(rec_path, "w"), indent=1, sort_keys=True)
+        for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+            if ("copy", cname) not in avg:
+                continue
+            factor = COPY_PROBE_BYTES / (avg[("copy", cname)] * 1024)
+            per_kernel = {fam: avg[(fam, cname)] * 1024 * factor for fam in CALL_KERNELS if (fam, cname) in avg}
+            if not per_kernel:
+                continue
+            entry[cname.lower() + "_factor"] = factor
+            entry[cname.lower() + "_bytes"] = sum(per_kernel.values())
+            entry[cname.lower() + "_bytes_per_kernel"] = per_kernel
+            lines.append(f"\n{cname}: the copy probe counts {avg[('copy', cname)]:.0f} KiB for "
+                         f"{COPY_PROBE_BYTES / 1024:.0f} KiB moved -> scale factor {factor:.4f}; per call "
+                         + ", ".join(f"{k} {v / 1e6:.2f} MB" for k, v in per_kernel.items()))
+        if "fetch_size_bytes" in entry or "write_size_bytes" in entry:
+            entry["kernel_sha256_16"] = kernel_hash()
+            entry["path"] = args.path
+            if "fetch_size_bytes" in entry and "write_size_bytes" in entry:
+                entry["bytes_per_launch"] = round(entry["fetch_size_bytes"] + entry["write_size_bytes"])
+                lines.append(f"\nrecorded {os.path.relpath(rec_path, ROOT)}: {entry['bytes_per_launch'] / 1e6:.2f} MB "
+                             f"per attention call (every kernel of the call)")
+            rec[key] = entry
+            json.dump(rec, open(rec_path, "w"), indent=1, sort_keys=True)
     print("\n".join(lines))
 
 
 def algorithmic_bytes(wl, live):
     """Bytes one attention launch (one layer, all streams) must move: the live
-    K and V windows, the queries and the outputs."""
+    K and V windows (live = keys attended per stream, a sequence), the queries
+    and the outputs."""
     e = 2
-    kv = wl.n_streams * wl.n_kv_heads * live * wl.head_dim * e * 2
+    kv = sum(wl.n_kv_heads * int(n) * wl.head_dim * e * 2 for n in live)
     q = wl.n_streams * wl.chunk * wl.n_q_heads * wl.head_dim * e
     return kv + 2 * q
 
@@ -170,8 +232,8 @@ def append_bytes(wl):
 def attention_flops(wl, live):
     # 4 * D * Hq * sum over queries of keys seen (QK^T and PV, 2 flops per MAC)
     c = wl.chunk
-    keys = sum(live - c + 1 + j for j in range(c))
-    return 4 * wl.head_dim * wl.n_q_heads * keys * wl.n_streams
+    keys = sum(int(n) - c + 1 + j for n in live for j in range(c))
+    return 4 * wl.head_dim * wl.n_q_heads * keys
 
 
 def kernel_hash():
@@ -215,15 +277,29 @@ def cpu_baseline(wl, seconds):
         n += 1
     dt = time.perf_counter() - t0
     pairs_per_step = wl.n_layers * wl.n_streams
+    # the same algorithmic bytes as the GPU figure: the bf16 K and V window of
+    # one (layer, stream) pair plus its queries and outputs, per call
+    call_bytes = w * hkv * d * 2 * 2 + 2 * c * hq * d * 2
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": round(n / dt / pairs_per_step, 6),
         "unit": "steps/s",
         "cores": threads,
         "kind": "oracle",
+        "gbps": round(n * call_bytes / dt / 1e9, 4),
+        "cpu_model": model,
         "sample": (f"{n} (layer, stream) attention calls of the float64 numpy oracle over a full "
                    f"W={w} window ({hq}/{hkv} heads, D={d}, {c} quer{'y' if c == 1 else 'ies'}) in "
-                   f"{dt:.1f} s; one step = {pairs_per_step} such calls; BLAS threads={threads}, "
-                   f"host cpus={len(os.sched_getaffinity(0))}"),
+                   f"{dt:.1f} s; one step = {pairs_per_step} such calls; gbps counts the bf16 cache "
+                   f"bytes of each call ({call_bytes} B), as the GPU figure does; BLAS threads={threads}, "
+                   f"host cpus={len(os.sched_getaffinity(0))}, {model}"),
     }
 
 
@@ -329,6 +405,9 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # live keys of every stream before the timed steps, from the bookkeeping
+    # (all layers of a stream hold the same count)
+    live0 = np.array([cache.get_state(0, b)[1] for b in range(B)], dtype=np.int64)
 
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -363,12 +442,19 @@ def main():
         n_launch = n_t * NL
         attn_ms = a0.elapsed_time(a1) / n_launch
 
-    live = w + F  # every stream holds a full window after pre-fill, after its prefix
-    bytes_launch = algorithmic_bytes(wl, live)
-    bytes_step = NL * (bytes_launch + append_bytes(wl))
+    # keys attended per stream at each timed call: the window after that
+    # call's append (plus the pinned prefix); the separate path's attention
+    # pass runs on the final windows
+    lives = [np.minimum(live0 + (i + 1) * c, w) + F for i in range(args.steps)]
+    if fused:
+        bytes_launch = float(np.mean([algorithmic_bytes(wl, lv) for lv in lives]))
+        flops_launch = float(np.mean([attention_flops(wl, lv) for lv in lives]))
+    else:
+        bytes_launch = algorithmic_bytes(wl, lives[-1])
+        flops_launch = attention_flops(wl, lives[-1])
+    bytes_step = NL * (float(np.mean([algorithmic_bytes(wl, lv) for lv in lives])) + append_bytes(wl))
     gbps_step = bytes_step * steps_per_s / 1e9
     achieved = bytes_launch / (attn_ms * 1e-3) / 1e9
-    flops_launch = attention_flops(wl, live)
     traffic = traffic_from_profiles(args.workload + (f"+prefix{F}" if F else ""))
 
     if args.copy_probe:
@@ -398,7 +484,7 @@ def main():
                                        else "seeded U[2^24-W,2^24)")},
         "kv_gbps": round(gbps_step, 1),
         "hbm_frac_step": round(gbps_step / HBM_PEAK_GBPS, 4),
-        "bytes_per_step": bytes_step,
+        "bytes_per_step": round(bytes_step),
         "roofline": {
             "bound": "hbm",
             "kernel": ("a8r_append_decode_attn (decode_mfma, fused append)" if fused and c == 1 else
@@ -409,7 +495,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "bytes_per_launch": bytes_launch,
+            "bytes_per_launch": round(bytes_launch),
             "avg_launch_ms": round(attn_ms, 5),
             "launches_timed": n_launch,
             "mfma_tflops": round(flops_launch / (attn_ms * 1e-3) / 1e12, 2),

@@ -6,10 +6,8 @@
  * are live, each new token overwrites the oldest one (the pair that is evicted).
  * Attention rotates keys and queries on read, by their index counted from the
  * window's current origin (the oldest live token), so query-key distances are
- * exact however large the absolute positions grow.  Stored K/V are never
- * modified after they are written.  (K is written in tile-phase form, rotated
- * once by its slot's offset in a 32-slot tile, which does not depend on the
- * origin; see a8r_cache_mode.)
+ * exact however large the absolute positions grow.  The ring holds K and V
+ * exactly as appended (a bit copy) and never modifies them.
  *
  * Passages this interface follows:
  *  - "Audio8 ASR Infinite: What It Actually Takes to Listen Forever", flowchart
@@ -80,14 +78,12 @@ typedef enum a8r_kernel_policy { A8R_KERNELS_AUTO = 0, A8R_KERNELS_PORTABLE = 1 
  * index ("Audio8 ASR Infinite: What It Actually Takes to Listen Forever",
  * section "Inside the Rolling KV Cache and Exact RoPE Re-Basing": re-basing
  * every surviving key to the new origin keeps relative distances exact).
- * Stored bits never change, so nothing accumulates.  Storage form (tile-phase
- * K): a key written to slot s is stored as R(s mod 32) k, computed in float32
- * (multiplies and adds without fusion) and rounded once to the cache dtype
- * (round to nearest even); values are stored as appended.  s mod 32 is fixed
- * for the token's lifetime, so this is written once and never redone; a read
- * at re-based index r = rho + (s mod 32) applies the remaining R(rho), which
- * the kernels fold into the query.  Pinned prefix token j sits at slot
- * offset j mod 32 the same way.
+ * Keys and values are stored exactly as appended and never change, so nothing
+ * accumulates.  A read at re-based index r applies R(r) in float32 with
+ * coefficients from a table built in float64 and rounded once to float32
+ * (the MFMA kernels split it as R(r - t) on the query and R(t) on the key,
+ * t = the key's offset in its 32-slot tile, and round the rotated key once,
+ * to the bf16 operand).
  *
  * A8R_REBASE_ON_EVICT (a comparison variant: the hazard the same page raises
  * there and in "Failure Modes That Only Appear on Day Three of a Session",
@@ -181,7 +177,7 @@ a8r_status a8r_append_prefix(a8r_cache* cache, int32_t layer, int32_t b0, int32_
  * for every session; "Audio8-ASR-Infinite-Compressed", Linux CPU notes).
  * a8r_export_prefix copies the n prefix tokens of streams [b0, b0+nb) in one
  * layer to k_out, v_out: device [nb][n][n_kv_heads][head_dim], 16-byte
- * aligned, K in its storage form (tile-phase keys), V as appended.  Every
+ * aligned, K and V as appended (the bits a8r_append_prefix took).  Every
  * stream in the range must hold exactly n >= 1 prefix tokens.
  * a8r_import_prefix takes exactly that output (same head count, head_dim and
  * dtype) and appends it to the prefixes of streams [b0, b0+nb) bit for bit;
@@ -270,8 +266,7 @@ a8r_status a8r_get_state(a8r_cache* cache, int32_t layer, int32_t b, int64_t* ne
                          int32_t* length, int32_t* next_slot);
 
 /* Copy the ring of one (layer, stream) pair to host, in physical slot order, K
- * in its storage form (tile-phase keys; with A8R_REBASE_ON_EVICT keys rotated
- * to their index), V as appended:
+ * and V as appended (with A8R_REBASE_ON_EVICT keys rotated to their index):
  * k_host, v_host: host [W][n_kv_heads][head_dim] dtype elements (either may be
  * NULL).  Synchronizes the stream.  For tests and tooling. */
 a8r_status a8r_read_ring(a8r_cache* cache, int32_t layer, int32_t b, void* k_host, void* v_host);

@@ -4,8 +4,8 @@
 // Device memory layout of one cache (all regions 256-byte aligned):
 //   K ring  [n_layers][n_streams][n_kv_heads][W_pad + F_pad][D]   row per slot:
 //            ring slots 0 .. W-1, then the pinned prefix from slot W_pad; a key
-//            is stored in tile-phase form R(slot mod 32) k (the rebase-on-evict
-//            variant: rotated to its re-based index)
+//            is stored as appended (the rebase-on-evict variant: rotated to
+//            its re-based index)
 //   V ring  [n_layers][n_streams][n_kv_heads][(W_pad + F_pad)/8][D][8]   8-slot
 //            blocks, transposed inside a block so 8 consecutive slots of one dim
 //            are 16 contiguous bytes (the k-operand layout of the PV MFMA)
@@ -90,11 +90,10 @@ hipError_t launch_reset(const Geometry& g, const StreamBatch& after, hipStream_t
 // append): rotates the new tokens' keys to their re-based indices and, where
 // the append evicted e tokens, every surviving key by R(-e), in place.
 hipError_t launch_rebase(const Geometry& g, int layer, const StreamBatch& before, int n, hipStream_t s);
-// Writes n tokens into the pinned prefix of a batch at prefix slots F .. F+n-1.
-// Appends n prefix tokens per stream: raw tokens tile-phase encoded (encode),
-// or keys already in that form (an import of a8r_export_prefix's output).
+// Copies n prefix tokens per stream into the pinned prefix of a batch, at
+// prefix slots F .. F+n-1 (an import of a8r_export_prefix's output is the same copy).
 hipError_t launch_append_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, const void* k,
-                                const void* v, bool encode, hipStream_t s);
+                                const void* v, hipStream_t s);
 // Copies the n prefix tokens of each stream out to k, v [nb][n][Hkv][D].
 hipError_t launch_export_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, void* k, void* v,
                                 hipStream_t s);

@@ -7,15 +7,13 @@
 // re-based index r and the query at index r_q are rotated (split-half RoPE,
 // "Audio8-ASR-Infinite-mlx", section "Requires a patched mlx-audio-swift";
 // theta from "Audio8-ASR-0.1B in audio.cpp", section "Architecture") on read;
-// the stored K/V bits are never rewritten.  K is stored in tile-phase form,
-// R(slot mod 32) k, written once (see phase_pair), so a read applies only the
-// origin-dependent rest of the rotation.
+// the stored K/V bits are never rewritten.  K and V are stored exactly as
+// appended (a bit copy); every read rotates the key by its re-based index.
 //
 // Kernels:
 //   reset_kernel       device record of the per-pair state after a reset
-//   append_kernel      writes new K/V rows into their ring slots (K in
-//                      tile-phase form; one block per stream) and records the
-//                      new state
+//   append_kernel      copies new K/V rows into their ring slots (one block
+//                      per stream) and records the new state
 //   attn_portable      any dtype / group size / chunk size; LDS-tiled VALU
 //   combine_kernel     merges split-K partials {m, l, O} of attn_portable,
 //                      and chunk_pipe
@@ -156,58 +154,12 @@ __device__ __forceinline__ void write_token_vals(const Geometry& g, int64_t pair
     store_token<EB>(g.k_ring, g.v_ring, g.pair_slots, g.d, pair, slot, c, kv, vv);
 }
 
-// Tile-phase storage of K.  A key written to slot s is stored as R(s mod 32) k:
-// rotated once, when it is written, by its offset in its 32-slot tile, and never
-// touched again.  A reader that visits the tile with base index rho (the key's
-// re-based index is rho + (s mod 32), plus W for a key behind the oldest slot on
-// the seam tile) then needs only R(rho), which it can apply to the query, since
-// <R(a) q, R(rho) R(t) k> = <R(a - rho) q, R(t) k>.  The stored value is the
-// rotation's exact float32 result rounded once to the cache dtype, the same
-// rounding a reader applies when it rotates a raw key into an MFMA operand.
-// Pairs (x1, x2) = dims (i, i + D/2) with (c, s) = table row t, pair i:
-// float32 multiplies and adds, no contraction (so every path and a float32
-// model of it store the same bits).
-__device__ __forceinline__ float2 phase_pair(float x1, float x2, float2 cs) {
-#pragma clang fp contract(off)
-    const float a = x1 * cs.x, b = x2 * cs.y, c = x2 * cs.x, d = x1 * cs.y;
-    return float2{a - b, c + d};
-}
-
-// Encodes the 16-byte K chunks lo (dims c*per16 ..) and hi (the same dims + D/2)
-// of one key with the pairs of table row `row` (a float2 row of D/2 pairs).
+// Copies 16-byte chunk c of one token's K and V rows (input layout
+// [nb][n][Hkv][D]) into `slot` of a pair, bit for bit.
 template <int EB>
-__device__ __forceinline__ void encode_chunks(const float2* row, int c, u32x4& lo, u32x4& hi) {
-    if constexpr (EB == 2) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float2 p0 = phase_pair(lo_bf16(lo[w]), lo_bf16(hi[w]), row[8 * c + 2 * w]);
-            const float2 p1 = phase_pair(hi_bf16(lo[w]), hi_bf16(hi[w]), row[8 * c + 2 * w + 1]);
-            lo[w] = (uint32_t)f32_to_bf16_bits(p0.x) | ((uint32_t)f32_to_bf16_bits(p1.x) << 16);
-            hi[w] = (uint32_t)f32_to_bf16_bits(p0.y) | ((uint32_t)f32_to_bf16_bits(p1.y) << 16);
-        }
-    } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float2 p = phase_pair(__uint_as_float(lo[w]), __uint_as_float(hi[w]), row[4 * c + w]);
-            lo[w] = __float_as_uint(p.x);
-            hi[w] = __float_as_uint(p.y);
-        }
-    }
-}
-
-// Writes token row j of the input ([nb][n][Hkv][D]) to `slot` of a pair: the
-// thread's K chunk c and its partner c + chunks/2 (tile-phase encoded unless
-// the keys are stored rotated to their index, A8R_REBASE_ON_EVICT), and the
-// same two V chunks as they are.
-template <int EB>
-__device__ __forceinline__ void write_token_pair(const Geometry& g, int64_t pair, int slot, int c, bool encode,
-                                                 const uint8_t* krow, const uint8_t* vrow) {
-    constexpr int per16 = 16 / EB;
-    const int half = g.d / per16 / 2;
-    u32x4 lo = *(const u32x4*)(krow + c * 16), hi = *(const u32x4*)(krow + (c + half) * 16);
-    if (encode) encode_chunks<EB>(g.table + (int64_t)(slot & (kTile - 1)) * (g.d / 2), c, lo, hi);
-    write_token_vals<EB>(g, pair, slot, c, lo, *(const u32x4*)(vrow + c * 16));
-    write_token_vals<EB>(g, pair, slot, c + half, hi, *(const u32x4*)(vrow + (c + half) * 16));
+__device__ __forceinline__ void write_token_chunk(const Geometry& g, int64_t pair, int slot, int c,
+                                                  const uint8_t* krow, const uint8_t* vrow) {
+    write_token_vals<EB>(g, pair, slot, c, *(const u32x4*)(krow + c * 16), *(const u32x4*)(vrow + c * 16));
 }
 
 // One block per stream; token j of stream b goes to slot (S + j) mod W.
@@ -218,15 +170,15 @@ __global__ __launch_bounds__(256) void append_kernel(Geometry g, int layer, Stre
     const int bi = blockIdx.x, b = st.b0 + bi;
     const int D = g.d, W = g.window;
     constexpr int per16 = 16 / EB;
-    const int halfc = D / per16 / 2;                   // chunk pairs per key
-    const int total = n_new * g.hkv * halfc;
+    const int chunks = D / per16;                      // 16-byte chunks per row
+    const int total = n_new * g.hkv * chunks;
     const int s0 = st.next_slot[bi];
     for (int t = threadIdx.x; t < total; t += blockDim.x) {
-        const int c = t % halfc;
-        const int rest = t / halfc;
+        const int c = t % chunks;
+        const int rest = t / chunks;
         const int kh = rest % g.hkv, j = rest / g.hkv;
         const int64_t src = (((int64_t)bi * n_new + j) * g.hkv + kh) * D * EB;
-        write_token_pair<EB>(g, pair_index(g, layer, b, kh), wrap_slot(s0 + j, W), c, !g.prerot, k + src, v + src);
+        write_token_chunk<EB>(g, pair_index(g, layer, b, kh), wrap_slot(s0 + j, W), c, k + src, v + src);
     }
     if (threadIdx.x == 0) {
         DevState ns;
@@ -238,33 +190,31 @@ __global__ __launch_bounds__(256) void append_kernel(Geometry g, int layer, Stre
 }
 
 // Pinned prefix: token j of stream b goes to prefix slot F + j (pair slot
-// w_pad + F + j, after the ring; never evicted).  Raw tokens are tile-phase
-// encoded like the ring's (phase (F + j) mod 32, the slot's offset in its
-// tile, since w_pad is a multiple of 32); an import (encode = false) writes
-// keys already in that form, as a8r_export_prefix returns them.
+// w_pad + F + j, after the ring; never evicted), copied bit for bit like a
+// ring token.  An import of a8r_export_prefix's output is the same copy.
 template <int EB>
 __global__ __launch_bounds__(256) void prefix_append_kernel(Geometry g, int layer, StreamBatch st, int n_new,
                                                             const uint8_t* __restrict__ k,
-                                                            const uint8_t* __restrict__ v, int encode) {
+                                                            const uint8_t* __restrict__ v) {
     const int bi = blockIdx.x, b = st.b0 + bi;
     const int D = g.d;
     constexpr int per16 = 16 / EB;
-    const int halfc = D / per16 / 2;
-    const int total = n_new * g.hkv * halfc;
+    const int chunks = D / per16;
+    const int total = n_new * g.hkv * chunks;
     const int f0 = st.prefix[bi];
     for (int t = threadIdx.x; t < total; t += blockDim.x) {
-        const int c = t % halfc;
-        const int rest = t / halfc;
+        const int c = t % chunks;
+        const int rest = t / chunks;
         const int kh = rest % g.hkv, j = rest / g.hkv;
         const int64_t src = (((int64_t)bi * n_new + j) * g.hkv + kh) * D * EB;
-        write_token_pair<EB>(g, pair_index(g, layer, b, kh), g.w_pad + f0 + j, c, encode != 0, k + src, v + src);
+        write_token_chunk<EB>(g, pair_index(g, layer, b, kh), g.w_pad + f0 + j, c, k + src, v + src);
     }
 }
 
 // Export of a pinned prefix: prefix token j of stream b back to row j of the
-// append layout [nb][n][Hkv][D]: K rows as stored (tile-phase encoded), V
+// append layout [nb][n][Hkv][D]: K rows as stored (the appended bits), V
 // gathered back out of its transposed 8-slot blocks.  An import
-// (prefix_append_kernel without encoding) restores exactly these bits.
+// (prefix_append_kernel) restores exactly these bits.
 template <int EB>
 __global__ __launch_bounds__(256) void prefix_export_kernel(Geometry g, int layer, StreamBatch st, int n,
                                                             uint8_t* __restrict__ k, uint8_t* __restrict__ v) {
@@ -406,9 +356,8 @@ hipError_t launch_combine(const Geometry& g, int nb, int n_q, int n_split, void*
 // Block = (split of the key range, KV head, stream) x (group of 64 query rows).
 // Rows are (query c, head-in-group hg) = c * G + hg.  Keys are walked in
 // re-based order r = 0 .. L-1 (slot = (oldest + r) mod W) in tiles of 16; each
-// tile's K rows are rotated to R(r) into LDS (a stored key already carries
-// R(slot mod 32), so it takes R(r - slot mod 32), the conjugate of row
-// |r - slot mod 32| when that is negative); scores, online softmax and PV run
+// tile's K rows are rotated by R(r) into LDS (table row r; the conjugate of row
+// |r| for a prefix key, r < 0); scores, online softmax and PV run
 // on VALU with 4 threads per row (4 keys of the tile each for the scores, a
 // quarter of the head dims each for PV).
 template <int D, int EB>
@@ -475,10 +424,10 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
                 const int slot = r < 0 ? g.w_pad + r + F : wrap_slot(oldest + r, W);
                 const float x1 = load_elem<EB>(kring, (int64_t)slot * D + i);
                 const float x2 = load_elem<EB>(kring, (int64_t)slot * D + i + NP);
-                // keys stored rotated to their index (A8R_REBASE_ON_EVICT) are used as they are
-                const int e = r - (slot & (kTile - 1));
-                float2 cs = g.prerot ? float2{1.f, 0.f} : g.table[(int64_t)(e < 0 ? -e : e) * NP + i];
-                if (e < 0) cs.y = -cs.y;
+                // R(r), the conjugate of row |r| for a prefix key (r < 0); keys
+                // stored rotated to their index (A8R_REBASE_ON_EVICT) are used as they are
+                float2 cs = g.prerot ? float2{1.f, 0.f} : g.table[(int64_t)(r < 0 ? -r : r) * NP + i];
+                if (r < 0) cs.y = -cs.y;
                 k1 = x1 * cs.x - x2 * cs.y;
                 k2 = x2 * cs.x + x1 * cs.y;
                 const int64_t vb = (int64_t)(slot >> 3) * D * 8 + (slot & 7);
@@ -552,9 +501,11 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 //
 // Rotation: with R(x) the split-half rotation by index x, the score is
 // <R(r_q) q, R(rho + t) k> = <R(r_q - rho) q, R(t) k> because rotations in each
-// 2-D plane compose additively and are orthogonal.  The ring stores R(t) k
-// (tile-phase form, written once by the append), so the visit's keys are MFMA
-// operands as they are, and only the query is rotated, once per visit, by
+// 2-D plane compose additively and are orthogonal.  The ring holds the keys as
+// appended; a lane always reads the same two offsets t of a tile (its MFMA
+// rows), so it keeps R(t) of those two rows in registers for the whole walk
+// and rotates its key rows by them on every visit (float32, one rounding to
+// the bf16 MFMA operand), while the query is rotated once per visit by
 // R(r_q - rho), a table row (< W + 32) fetched with the visit's keys.  On the
 // first visit the newest keys (offsets before the oldest slot, index
 // rho + t + W) take a second query rotation R(r_q - rho - W), composed in
@@ -771,7 +722,7 @@ __device__ __forceinline__ void dec_load_v(const DecodeCtx& c, int k, unsigned c
 // A visit's K part copied from LDS into registers: the query-rotation pairs
 // R(r_q - rho) and the lane's two K rows (tb0, tb1; dims 8*gq + 32*kk + e), so
 // that the buffer can be refilled before the arithmetic starts.  The rows are
-// MFMA operands as they are: a stored key already carries R(t).
+// the keys as appended; dec_scores rotates them by R(tb0), R(tb1).
 template <int D>
 struct DecK {
     float4 qc[D / 64][4];
@@ -793,8 +744,11 @@ __device__ __forceinline__ void dec_read_k(const DecodeCtx& c, const unsigned ch
 // Scores of visit k from its K part and the online-softmax update; returns
 // this lane's eight probabilities (keys 8*gq .. 8*gq+7, head n) as bf16.
 // SEAM: k may be the ring's first visit (only a wave's first visit can be).
+// kcr: R(tb0) and R(tb1) for the lane's pairs (table rows tb0, tb1; unused
+// when the keys are stored rotated to their index).
 template <int D, bool SEAM>
 __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const DecK<D>& r,
+                                             const float4 (&kcr)[2][D / 64][4],
                                              const u32x4 (&qraw)[D / 32], const unsigned char* lds_rw,
                                              floatx4 (&o)[D / 16], float& m, float& l) {
     constexpr int KK = D / 32, NB = D / 16;
@@ -802,12 +756,23 @@ __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const De
     const int s0 = vs.s0, rho = vs.rho;
     bf16x8 qb[KK];
     rotate_row<D>(r.qc, qraw, qb);            // query by R(r_q - rho)
+    bf16x8 ka[KK], kb[KK];                    // key rows tb0, tb1 by R(tb0), R(tb1)
+    if (!c.prerot) {
+        rotate_row<D>(kcr[0], r.k0, ka);
+        rotate_row<D>(kcr[1], r.k1, kb);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            ka[kk] = __builtin_bit_cast(bf16x8, r.k0[kk]);
+            kb[kk] = __builtin_bit_cast(bf16x8, r.k1[kk]);
+        }
+    }
     const bool seam = SEAM && (k == 0) && (c.t_o > 0);
     floatx4 sc0 = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-        sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k0[kk]), qb[kk], sc0, 0, 0, 0);
-        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k1[kk]), qb[kk], sc1, 0, 0, 0);
+        sc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qb[kk], sc0, 0, 0, 0);
+        sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qb[kk], sc1, 0, 0, 0);
     }
     if (seam && !c.prerot) {
         // the seam visit (wave-uniform): keys behind the oldest slot sit W
@@ -835,8 +800,8 @@ __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const De
         floatx4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            w0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k0[kk]), qbw[kk], w0, 0, 0, 0);
-            w1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k1[kk]), qbw[kk], w1, 0, 0, 0);
+            w0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qbw[kk], w0, 0, 0, 0);
+            w1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qbw[kk], w1, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {                 // element j: keys 8 gq + j and 8 gq + 4 + j
@@ -1019,11 +984,27 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     const int per = (n_visit + n_split - 1) / n_split;
     const int k0 = split * per, k1 = min(n_visit, k0 + per);
 
+    // R(tb0), R(tb1) for this lane's pairs (table rows < 32, L2-resident),
+    // kept in registers for the whole walk (staging them in LDS and reading
+    // them per visit was 0.6 us per launch slower at the 64-stream 3B shape);
+    // the oldest loads of the kernel, so every explicit wait below covers them
+    float4 kcr[2][D / 64][4];
+    if (!PREROT) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float4* row = (const float4*)(g.table + (int64_t)(h ? c.tb1 : c.tb0) * (D / 2)) + 4 * gq;
+#pragma unroll
+            for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kcr[h][kk][j] = row[16 * kk + j];
+        }
+    }
+
     // Fused append: the wave whose visits include the new token's tile (visit
-    // k_tok) loads the token into LDS with its prologue, tile-phase encodes its
-    // K row there, patches it into its LDS copy of that tile once the tile has
-    // landed, and writes it into the ring slot after the walk, so nothing waits
-    // for a store (no other wave or block reads that slot in this call).
+    // k_tok) loads the token into LDS with its prologue, patches it into its
+    // LDS copy of that tile once the tile has landed, and writes it into the
+    // ring slot after the walk, so nothing waits for a store (no other wave or
+    // block reads that slot in this call).
     int k_tok = -1;
     const int t_tok = s_prev & (kTile - 1);
     if (fused) {
@@ -1031,14 +1012,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         if (kv < 0) kv += c.n_tiles;
         if (kv >= k0 && kv < k1 && (kv - k0) % 4 == wave) {
             // at most one wave per block: the token's K row to lds_tok[0, 2D),
-            // its V row to [2D, 4D), table row t_tok to [4D, 8D) (other lanes
-            // re-read the K row's start)
+            // its V row to [2D, 4D) (other lanes re-read the K row's start)
             k_tok = kv;
             const int64_t src = ((int64_t)bi * g.hkv + kh) * D;
             const void* from = lane < D / 8   ? (const void*)(k_new + src + 8 * lane)
                              : lane < D / 4   ? (const void*)(v_new + src + 8 * (lane - D / 8))
-                             : lane < D / 2   ? (const void*)((const unsigned char*)(g.table + (int64_t)t_tok * (D / 2)) +
-                                                              16 * (lane - D / 4))
                                               : (const void*)(k_new + src);
             dma16(from, lds_tok + 16 * lane);
         }
@@ -1080,14 +1058,6 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qraw[kk] = *(const u32x4*)(qrow + 64 * kk);
     }
-    // the new token's K row in tile-phase form R(t_tok) k (the wave that owns it)
-    if (k_tok >= 0 && !c.prerot && lane < D / 16) {
-        u32x4* tk = (u32x4*)lds_tok;
-        u32x4 lo = tk[lane], hi = tk[lane + D / 16];
-        encode_chunks<2>((const float2*)(lds_tok + 4 * D), lane, lo, hi);
-        tk[lane] = lo;
-        tk[lane + D / 16] = hi;
-    }
 
     floatx4 o[NB];
 #pragma unroll
@@ -1122,7 +1092,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         dec_read_k<D>(c, ka, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);                                 // copied out of ka
         if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, ka);
-        bf16x8 pb = dec_scores<D, true>(c, k, rk, qraw, lds_rw, o, m, l);
+        bf16x8 pb = dec_scores<D, true>(c, k, rk, kcr, qraw, lds_rw, o, m, l);
         wait_v(k);
         if (k == k_tok) patch_v<D>(va, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(va, lane, rv);
@@ -1136,7 +1106,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         dec_read_k<D>(c, kb, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, kb);
-        pb = dec_scores<D, false>(c, k, rk, qraw, lds_rw, o, m, l);
+        pb = dec_scores<D, false>(c, k, rk, kcr, qraw, lds_rw, o, m, l);
         wait_v(k);
         if (k == k_tok) patch_v<D>(vb, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(vb, lane, rv);
@@ -1309,10 +1279,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
 // for the whole walk, and each wave issues a quarter of every visit's loads
 // (LDS DMA).
 // Rotation: each query row is rotated once, by its own re-based index
-// r_q(c) = L - C + c; key t of a visit, stored as R(t) k (tile-phase form), by
-// R(rho), the table row staged with the visit.  On the first visit rho = -t_o
-// (R(t_o) conjugated), and the window's newest keys that share the oldest key's
-// tile (t < t_o, index t - t_o + W) get R(W) composed on top.  Query c sees
+// r_q(c) = L - C + c; key t of a visit (stored as appended) by R(rho + t),
+// composed in float32 from R(rho), the table row staged with the visit, and
+// R(t), which the lane that rotates key t keeps in registers.  On the first
+// visit rho = -t_o (R(t_o) conjugated), and the window's newest keys that share
+// the oldest key's tile (t < t_o, index t - t_o + W) get R(W) composed on top.  Query c sees
 // keys with index <= r_q(c): causal inside the chunk, the whole older window
 // before it.  With several splits each block writes its rows' partials
 // {m, l, O} and combine_kernel, launched next, merges them (a chip-wide merge
@@ -1447,6 +1418,10 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     // first wait below is unconditional.
     const int kr_t = 8 * wave + (lane >> 3);           // key offset this lane rotates
     const int kr_i = P * (lane & 7);                   // its first pair index
+    // R(kr_t) for those pairs, for the whole walk (table row kr_t < 32)
+    float2 rt[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) rt[i] = g.table[(int64_t)kr_t * (D / 2) + kr_i + i];
     u32x4 qr[NW][KK];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -1465,8 +1440,8 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         dma16((const unsigned char*)(g.table + (int64_t)c.rq * (D / 2)) + off, lds_qc + wave_b * 1024);
     }
     // Fused append (one row group): the new tokens of this (stream, KV head)
-    // whose tiles are among this block's visits are written into their ring
-    // slots, tile-phase encoded as append_kernel writes them, and the block
+    // whose tiles are among this block's visits are copied into their ring
+    // slots, as append_kernel writes them, and the block
     // waits for the stores (and the query and table loads above, issued first
     // so that their latency overlaps) before its first K/V load.  No other
     // block reads those tiles in this call.
@@ -1481,15 +1456,15 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
             mine = mine || (v >= k0 && v < k1);
         }
         if (mine) {
-            constexpr int halfc = D / 16;              // chunk pairs of a bf16 row
-            for (int t = tid; t < C * halfc; t += 256 * WG) {
-                const int j = t / halfc, cc = t - j * halfc;
+            constexpr int chunks = D / 8;              // 16-byte chunks of a bf16 row
+            for (int t = tid; t < C * chunks; t += 256 * WG) {
+                const int j = t / chunks, cc = t - j * chunks;
                 const int slot = wrap_slot(s_prev + j, W);
                 const int v = visit_of(slot);
                 if (v >= k0 && v < k1) {
                     const int64_t src = (((int64_t)bi * C + j) * g.hkv + kh) * D * 2;
-                    write_token_pair<2>(g, pair, slot, cc, true, (const uint8_t*)k_new + src,
-                                        (const uint8_t*)v_new + src);
+                    write_token_chunk<2>(g, pair, slot, cc, (const uint8_t*)k_new + src,
+                                         (const uint8_t*)v_new + src);
                 }
             }
             __builtin_amdgcn_s_waitcnt(0);             // the tokens are in the L2 ...
@@ -1525,12 +1500,11 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     const int r_last = L - 1;
 
     // Rotates key kr_t of local visit v (pairs kr_i .. kr_i + P - 1) from its K
-    // slot into a rotated tile.  The stored key already carries R(t) (tile-phase
-    // form), so it takes R(rho): the visit's staged row, conjugated where rho < 0
-    // (the ring's first visit, rho = -t_o, and prefix visits); on the first
-    // visit keys before the oldest slot (the window's newest) get R(W) on top.
-    // The rotated key is rounded to bf16 once more (the stored form was
-    // rounded once already).
+    // slot into a rotated tile, by R(rho + kr_t): the visit's staged row R(rho),
+    // conjugated where rho < 0 (the ring's first visit, rho = -t_o, and prefix
+    // visits; on the first visit keys before the oldest slot, the window's
+    // newest, get R(W) on top), composed with the lane's R(kr_t).  The key is
+    // rounded to bf16 once, as the MFMA operand.
     auto rotate = [&](const unsigned char* kslot, unsigned char* tile, bool first, bool seam) {
         const float4* br = (const float4*)(kslot + PB::kK) + kr_i / 2;
         const unsigned char* kraw = kslot + kr_t * D * 2;
@@ -1572,6 +1546,11 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
                     cf[2 * i2 + h] = wrap ? r : a;
                 }
             }
+        }
+#pragma unroll
+        for (int i = 0; i < P; ++i) {                  // then R(kr_t): angles add
+            const float2 a = cf[i], t = rt[i];
+            cf[i] = float2{a.x * t.x - a.y * t.y, a.y * t.x + a.x * t.y};
         }
         __bf16 y1[P], y2[P];
 #pragma unroll
@@ -1931,13 +1910,13 @@ hipError_t launch_append(const Geometry& g, int layer, const StreamBatch& before
 }
 
 hipError_t launch_append_prefix(const Geometry& g, int layer, const StreamBatch& st, int n, const void* k,
-                                const void* v, bool encode, hipStream_t s) {
+                                const void* v, hipStream_t s) {
     if (g.elem_bytes == 2)
         hipLaunchKernelGGL(prefix_append_kernel<2>, dim3(st.nb), dim3(256), 0, s, g, layer, st, n,
-                           (const uint8_t*)k, (const uint8_t*)v, encode ? 1 : 0);
+                           (const uint8_t*)k, (const uint8_t*)v);
     else
         hipLaunchKernelGGL(prefix_append_kernel<4>, dim3(st.nb), dim3(256), 0, s, g, layer, st, n,
-                           (const uint8_t*)k, (const uint8_t*)v, encode ? 1 : 0);
+                           (const uint8_t*)k, (const uint8_t*)v);
     return hipGetLastError();
 }
 
