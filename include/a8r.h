@@ -232,6 +232,23 @@ a8r_status a8r_decode_attn(a8r_cache* cache, int32_t layer, int32_t b0, int32_t 
 a8r_status a8r_chunk_attn(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb,
                           int32_t n_new, const void* q, void* out);
 
+/* a8r_chunk_attn for callers that cannot allocate device memory, or must not
+ * depend on a workspace region: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, preconditions and
+ * results as a8r_chunk_attn (bit for bit), except n_new >= 2; the kernels'
+ * split partials live in one static device array of the library (64 MiB per
+ * GPU, held until the process ends) instead of the cache's workspace.  A call
+ * needs min(nb, 128) * n_kv_heads * 16 * n_new * group * (head_dim + 2) * 4
+ * bytes of it (rounded up to 256 at the boundary of the two parts) when
+ * n_new <= 16, none above; more than 64 MiB is rejected with EINVAL before any
+ * side effect.  Allocates nothing (the array's address is looked up once per
+ * device).  Every call on a GPU shares that GPU's array, which keeps the last
+ * call's contents; calls that overlap on one GPU (other streams, other caches)
+ * race and must be ordered by the caller.
+ * Errors: as a8r_chunk_attn; EINVAL also for n_new < 2 or the size above. */
+a8r_status a8r_chunk_attn_static(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb,
+                                 int32_t n_new, const void* q, void* out);
+
 /* The decode step of an audio clock in one call: exactly a8r_append_kv with
  * n_new = 1 followed by a8r_decode_attn on the same streams, executed as a
  * single kernel (the new token's K/V are written into the ring by the same

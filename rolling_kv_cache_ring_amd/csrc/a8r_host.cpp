@@ -469,6 +469,43 @@ a8r_status a8r_chunk_attn(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, i
     return attention_call(c, layer, b0, nb, n_new, q, out);
 }
 
+a8r_status a8r_chunk_attn_static(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n_new,
+                                 const void* q, void* out) {
+    a8r_status st = check_attention(c, layer, b0, nb, n_new, 0, q, out);
+    if (st != A8R_OK) return st;
+    if (n_new < 2) return fail(A8R_EINVAL, "n_new %d < 2 (one query per stream is a8r_decode_attn)", n_new);
+    // split partials of one launch (up to kBatch streams), laid out as the
+    // cache's own: [stream][kv head][kMaxSplits][row][D] float32, then (m, l)
+    const a8r::Geometry& cg = c->geo;
+    const size_t rows = (size_t)n_new * cg.group;
+    const size_t nbl = (size_t)std::min(nb, a8r::kBatch);
+    const size_t o_bytes =
+        a8r::align_up(nbl * cg.hkv * a8r::kMaxSplits * rows * cg.d * sizeof(float), a8r::kAlign);
+    const size_t need = n_new <= a8r::kMaxPartialQ ? o_bytes + nbl * cg.hkv * a8r::kMaxSplits * rows * 2 * sizeof(float)
+                                                   : 0;
+    if (need > a8r::kStaticScratchBytes)
+        return fail(A8R_EINVAL,
+                    "a8r_chunk_attn_static: %d streams x %d KV heads x %d query rows need %zu bytes of split "
+                    "partials, more than the %zu-byte static scratch (use fewer streams per call)",
+                    (int)nbl, cg.hkv, (int)rows, need, a8r::kStaticScratchBytes);
+    void* base = nullptr;
+    hipError_t e = a8r::static_scratch(c->device, &base);
+    if (e != hipSuccess) return fail(A8R_EDEVICE, "static scratch address: %s", hipGetErrorString(e));
+    a8r::Geometry g = cg;
+    g.rows_max = (int)rows;
+    g.part_o = (float*)base;
+    g.part_ml = (float*)((uint8_t*)base + o_bytes);
+    const size_t qrow = (size_t)n_new * c->cfg.n_q_heads * c->cfg.head_dim * c->geo.elem_bytes;
+    for (int32_t i0 = 0; i0 < nb; i0 += a8r::kBatch) {
+        a8r::StreamBatch sb;
+        fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
+        e = a8r::launch_attention(g, layer, sb, n_new, (const uint8_t*)q + i0 * qrow, (uint8_t*)out + i0 * qrow,
+                                  c->cfg.kernel_policy == A8R_KERNELS_AUTO, c->n_cu, c->stream);
+        if (e != hipSuccess) return device_fail(c, e, "attention kernel");
+    }
+    return ok();
+}
+
 a8r_status a8r_append_decode_attn(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, const void* k,
                                   const void* v, const void* q, void* out, int32_t* slots_out,
                                   int64_t* evicted_out) {

@@ -40,6 +40,8 @@ constexpr int kBatch = 128;        // streams per launch (their state travels in
 constexpr int kMaxGroupMfma = 16;   // query heads per KV head in the MFMA decode kernel
 constexpr uint64_t kSlotEmpty = ~(uint64_t)0;   // an exchange slot holding no partial
 constexpr int kXSlots = kMaxSplits - 1;         // exchange-slot rows per pair: the nodes of a merge tree
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;   // a8r_chunk_attn_static's split partials, per GPU
+constexpr int kMaxDevices = 64;
 
 struct DevState {
     int64_t next_pos;   // absolute position of the next token
@@ -108,6 +110,9 @@ hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now
 hipError_t launch_append_decode(const Geometry& g, int layer, const StreamBatch& before,
                                 const void* k, const void* v, const void* q, void* out,
                                 bool allow_mfma, int n_cu, hipStream_t s);
+// The device address of the library's static scratch array (kStaticScratchBytes,
+// 256-byte aligned) on `device`, looked up once per device and kept.
+hipError_t static_scratch(int device, void** ptr);
 // n new tokens per stream appended and attended in one launch where the MFMA
 // chunk kernel runs with one row group (else append + attention).
 hipError_t launch_append_chunk(const Geometry& g, int layer, const StreamBatch& before, int n,

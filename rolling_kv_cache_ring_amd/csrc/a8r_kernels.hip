@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <mutex>
 #include <type_traits>
 #include <stdint.h>
 #include <stdlib.h>
@@ -1890,6 +1891,37 @@ bool mfma_chunk_ok(const Geometry& g, int n_q) {
 }
 
 }  // namespace
+
+// ======================================================== static scratch ==
+// Split partials of a8r_chunk_attn_static, for callers that cannot allocate:
+// one array per GPU, alive until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): the address comes from hipGetSymbolAddress, once per device with
+// that device current, and goes into the Geometry the kernels take.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(int device, void** ptr) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != device) e = hipSetDevice(device);
+        if (e != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != device) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        addr[device] = p;
+    }
+    *ptr = addr[device];
+    return hipSuccess;
+}
 
 // ================================================================ launchers ==
 hipError_t launch_reset(const Geometry& g, const StreamBatch& after, hipStream_t s) {
