@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 
 import numpy as np
 
@@ -289,7 +290,14 @@ class Cache:
             cache_destroy(self.handle)
             self.handle = None
 
-    __del__ = close
+    def __del__(self):
+        # a cache still open when the interpreter shuts down is left to the
+        # process exit: the HIP runtime may already be gone, and destroy
+        # synchronizes a stream and frees device memory
+        if sys.is_finalizing():
+            self.handle = None
+            return
+        self.close()
 
     def set_stream(self, stream):
         set_stream(self.handle, stream)
