@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--prefix", type=int, default=0, metavar="F",
                     help="pin an F-token prompt prefix in every (layer, stream) before the pre-fill; "
                          "attention then covers F + W keys")
+    ap.add_argument("--rebuild", action="store_true",
+                    help="after the timed steps, also time window re-prefill (a8r_rebuild_window): every "
+                         "stream's window of every layer re-derived from stored hidden states (hidden size "
+                         "q_heads x head_dim) with synthetic projection weights, beside the ring's per-step cost")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -303,6 +307,61 @@ def cpu_baseline(wl, seconds):
     }
 
 
+def rebuild_timing(args, torch, cache, wl, ring_ms_per_step, gen):
+    """Window re-prefill beside the ring: every stream's window of every layer
+    re-derived from stored hidden states [B][W][hidden] (one buffer, re-read
+    for each layer) with seeded synthetic weights, as a8r_rebuild_window calls;
+    3 warm-up layers, then 2 full rebuilds (all layers) timed with HIP events."""
+    import rolling_kv_cache_ring_amd as a8r
+    B, NL, hq, hkv, d, w = wl.n_streams, wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.window
+    hidden = hq * d
+    bf = torch.bfloat16
+    h = torch.randn((B, w, hidden), device="cuda", generator=gen).to(bf).view(torch.int16)
+    wk = (torch.randn((hkv * d, hidden), device="cuda", generator=gen) * hidden ** -0.5).to(bf).view(torch.int16)
+    wv = (torch.randn((hkv * d, hidden), device="cuda", generator=gen) * hidden ** -0.5).to(bf).view(torch.int16)
+    L = a8r.lib()
+    stream = torch.cuda.current_stream()
+
+    def one(layer):
+        st = L.a8r_rebuild_window(cache.handle, layer, 0, B, w, hidden, h.data_ptr(), wk.data_ptr(), wv.data_ptr())
+        if st:
+            raise a8r.A8RError(st, L.a8r_last_error().decode())
+
+    # every stream at least W positions in (a rebuilt window holds the last W
+    # positions); the ring's own measurement is done by now
+    cache.reset(0, [cache.get_state(0, b)[0] + w for b in range(B)])
+    for layer in range(3):
+        one(layer)
+    torch.cuda.synchronize()
+    reps = 2
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        for layer in range(NL):
+            one(layer)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_full = e0.elapsed_time(e1) / reps
+    ms_layer = ms_full / NL
+    flops_layer = 2.0 * B * w * hidden * (2 * hkv * d)
+    bytes_layer = B * w * hidden * 2 + 2 * hkv * d * hidden * 2 + 2 * B * w * hkv * d * 2
+    del h, wk, wv
+    return {
+        "hidden_dim": hidden,
+        "tokens_per_stream": w,
+        "ms_per_layer": round(ms_layer, 4),
+        "ms_per_full_rebuild": round(ms_full, 3),
+        "tflops": round(flops_layer / (ms_layer * 1e-3) / 1e12, 1),
+        "mfma_frac_bf16_dense": round(flops_layer / (ms_layer * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4),
+        "hbm_gbps": round(bytes_layer / (ms_layer * 1e-3) / 1e9, 1),
+        "ring_ms_per_step": round(ring_ms_per_step, 5),
+        "full_rebuild_over_ring_step": round(ms_full / ring_ms_per_step, 1),
+        "amortized_ms_per_step_rebuilt_every_W_steps": round(ms_full / w, 5),
+        "note": ("window re-prefill of the K/V projections only: a decoder's re-prefill also recomputes "
+                 "the hidden states through every layer below, which this does not count"),
+    }
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -457,6 +516,8 @@ def main():
     achieved = bytes_launch / (attn_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(args.workload + (f"+prefix{F}" if F else ""))
 
+    rebuild = rebuild_timing(args, torch, cache, wl, ms, gen) if args.rebuild else None
+
     if args.copy_probe:
         copy_probe(torch)
 
@@ -504,6 +565,8 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
+    if rebuild:
+        line["rebuild"] = rebuild
     if rebase:
         # the variant's extra work: every eviction re-rotates the whole K window
         # (read + write), per layer and step at full windows

@@ -275,6 +275,26 @@ a8r_status a8r_append_chunk_attn(a8r_cache* cache, int32_t layer, int32_t b0, in
                                  const void* k, const void* v, const void* q, void* out, int32_t* slots_out,
                                  int64_t* evicted_out);
 
+/* Window re-prefill, the comparison the scope table's last row asks for: the
+ * window of streams [b0, b0+nb) in `layer` is rebuilt from stored hidden
+ * states, the way "audio8-asr-infinite-p150" (section "Limitations") rebuilds
+ * its decoder's rolling context by re-prefilling instead of trimming.  For each
+ * stream, K = H Wk^T and V = H Wv^T over the n tokens of H:
+ *   hidden: device [nb][n][hidden_dim] bf16, the window's tokens oldest first;
+ *   w_k, w_v: device [n_kv_heads * head_dim][hidden_dim] bf16 (a linear
+ *   layer's weight layout, no bias); output column kh * head_dim + d is
+ *   element d of KV head kh.
+ * Each result is a float32 accumulation of bf16 products rounded once to bf16
+ * (nearest even).  The n tokens become the window: the positions P-n .. P-1
+ * (P unchanged), token j in ring slot j, L = n, next slot n mod W; a pinned
+ * prefix is kept.  16-byte aligned pointers, 1 <= n <= W, n <= P,
+ * hidden_dim a multiple of 64 (at most 65536).  Asynchronous on the cache's
+ * stream.  Errors: EINVAL, EUNSUPPORTED (float32 caches, A8R_REBASE_ON_EVICT,
+ * n_kv_heads * head_dim not a multiple of 128), EDEVICE; nothing changes on
+ * error. */
+a8r_status a8r_rebuild_window(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb, int32_t n,
+                              int32_t hidden_dim, const void* hidden, const void* w_k, const void* w_v);
+
 /* Read the state of one (layer, stream) pair: next position P, live count L,
  * next slot S (host outputs, any may be NULL).  Synchronizes the stream and
  * checks the device-side copy against the host bookkeeping; a mismatch returns

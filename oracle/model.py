@@ -90,6 +90,25 @@ class OracleCache:
             evicted.append(e)
         return slots, evicted
 
+    def rebuild(self, layer: int, b0: int, k: np.ndarray, v: np.ndarray) -> None:
+        """Window re-prefill: k, v [nb, n, Hkv, D] (oldest first) become each
+        stream's window, the last n positions (P unchanged), token j in slot j,
+        the next token in slot n mod W ("audio8-asr-infinite-p150", section
+        "Limitations"; see prefill.py).  The pinned prefix is kept."""
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        nb, n = k.shape[:2]
+        if not 1 <= n <= self.window:
+            raise ValueError("n out of [1, W]")
+        for i in range(nb):
+            led, ring_k, ring_v = self._pair(layer, b0 + i)
+            if led.next_pos < n:
+                raise ValueError("the window would start before position 0")
+            ring_k[:n] = k[i]
+            ring_v[:n] = v[i]
+            led.length = n
+            led.next_slot = n % self.window
+
     def append_prefix(self, layer: int, b0: int, k: np.ndarray, v: np.ndarray) -> None:
         """Pin k, v [nb, n_new, Hkv, D] after each stream's prefix (its window must be empty)."""
         k = np.asarray(k, dtype=np.float64)

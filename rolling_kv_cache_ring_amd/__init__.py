@@ -32,7 +32,7 @@ EXPORTED = [
     "a8r_workspace_bytes", "a8r_cache_create", "a8r_cache_destroy", "a8r_set_stream", "a8r_reset",
     "a8r_append_kv", "a8r_decode_attn", "a8r_chunk_attn", "a8r_chunk_attn_static", "a8r_append_decode_attn",
     "a8r_append_chunk_attn",
-    "a8r_get_state", "a8r_read_ring", "a8r_append_prefix", "a8r_export_prefix", "a8r_import_prefix", "a8r_clear_prefix",
+    "a8r_get_state", "a8r_read_ring", "a8r_rebuild_window", "a8r_append_prefix", "a8r_export_prefix", "a8r_import_prefix", "a8r_clear_prefix",
     "a8r_prefix_length",
     "a8r_last_error", "a8r_ledger_create", "a8r_ledger_destroy", "a8r_ledger_reset",
     "a8r_ledger_append", "a8r_ledger_get", "a8r_version",
@@ -99,6 +99,9 @@ def lib():
     L.a8r_chunk_attn_static.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         _c_void_p, _c_void_p]
     L.a8r_chunk_attn_static.restype = st
+    L.a8r_rebuild_window.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, _c_void_p, _c_void_p, _c_void_p]
+    L.a8r_rebuild_window.restype = st
     L.a8r_append_decode_attn.argtypes = [_c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32p, _i64p]
     L.a8r_append_decode_attn.restype = st
@@ -236,6 +239,11 @@ def chunk_attn_static(handle: int, layer: int, b0: int, nb: int, n_new: int, q, 
     _check(lib().a8r_chunk_attn_static(handle, layer, b0, nb, n_new, _ptr(q), _ptr(out)))
 
 
+def rebuild_window(handle: int, layer: int, b0: int, nb: int, n: int, hidden_dim: int, hidden, w_k, w_v) -> None:
+    """a8r_rebuild_window: the window re-derived from stored hidden states."""
+    _check(lib().a8r_rebuild_window(handle, layer, b0, nb, n, hidden_dim, _ptr(hidden), _ptr(w_k), _ptr(w_v)))
+
+
 def append_decode_attn(handle: int, layer: int, b0: int, nb: int, k, v, q, out, want_bookkeeping=True):
     """a8r_append_kv (one token per stream) + a8r_decode_attn in one launch."""
     if want_bookkeeping:
@@ -316,6 +324,9 @@ class Cache:
 
     def chunk_attn_static(self, layer, b0, nb, n_new, q, out):
         chunk_attn_static(self.handle, layer, b0, nb, n_new, q, out)
+
+    def rebuild_window(self, layer, b0, nb, n, hidden_dim, hidden, w_k, w_v):
+        rebuild_window(self.handle, layer, b0, nb, n, hidden_dim, hidden, w_k, w_v)
 
     def append_decode_attn(self, layer, b0, nb, k, v, q, out, want_bookkeeping=True):
         return append_decode_attn(self.handle, layer, b0, nb, k, v, q, out, want_bookkeeping)

@@ -94,6 +94,16 @@ struct Ledger {
         }
     }
 
+    // Window rebuilt from n tokens (the last n positions, P unchanged), held in
+    // slots 0 .. n-1.
+    void rebuild(int32_t layer, int32_t b0, int32_t nb, int32_t n) {
+        for (int32_t i = 0; i < nb; ++i) {
+            PairState& s = at(layer, b0 + i);
+            s.length = n;
+            s.next_slot = n == window ? 0 : n;
+        }
+    }
+
     a8r_status check_reset(int32_t b0, int32_t nb, const int64_t* next_pos, const int32_t* next_slot) const {
         if (nb < 1 || b0 < 0 || b0 > n_streams - nb)
             return fail(A8R_EINVAL, "streams [%d, %d+%d) out of [0, %d)", b0, b0, nb, n_streams);
@@ -552,6 +562,38 @@ a8r_status a8r_append_chunk_attn(a8r_cache* c, int32_t layer, int32_t b0, int32_
         if (e != hipSuccess) return device_fail(c, e, "append+chunk kernel");
     }
     c->ledger.append(layer, b0, nb, n_new, slots_out, evicted_out);
+    return ok();
+}
+
+a8r_status a8r_rebuild_window(a8r_cache* c, int32_t layer, int32_t b0, int32_t nb, int32_t n, int32_t hidden_dim,
+                              const void* hidden, const void* w_k, const void* w_v) {
+    a8r_status st = check_live(c);
+    if (st != A8R_OK) return st;
+    if ((st = check_streams(c, layer, b0, nb)) != A8R_OK) return st;
+    if (c->geo.elem_bytes != 2) return fail(A8R_EUNSUPPORTED, "window rebuild needs a bf16 cache");
+    if (c->geo.prerot) return fail(A8R_EUNSUPPORTED, "window rebuild is not available with A8R_REBASE_ON_EVICT");
+    if ((c->geo.hkv * c->geo.d) % 128)
+        return fail(A8R_EUNSUPPORTED, "window rebuild needs n_kv_heads * head_dim %% 128 == 0 (got %d)",
+                    c->geo.hkv * c->geo.d);
+    if (n < 1 || n > c->cfg.window) return fail(A8R_EINVAL, "n %d out of [1, W=%d]", n, c->cfg.window);
+    if (hidden_dim < 64 || hidden_dim % 64 || hidden_dim > (1 << 16))
+        return fail(A8R_EINVAL, "hidden_dim %d must be a positive multiple of 64, at most 65536", hidden_dim);
+    if (!hidden || !w_k || !w_v) return fail(A8R_EINVAL, "hidden, w_k or w_v is NULL");
+    if (!aligned16(hidden) || !aligned16(w_k) || !aligned16(w_v))
+        return fail(A8R_EINVAL, "hidden, w_k and w_v must be 16-byte aligned");
+    for (int32_t i = 0; i < nb; ++i)
+        if (c->ledger.at(layer, b0 + i).next_pos < n)
+            return fail(A8R_EINVAL, "stream %d layer %d: next position %lld < n = %d (window before position 0)",
+                        b0 + i, layer, (long long)c->ledger.at(layer, b0 + i).next_pos, n);
+    const size_t row = (size_t)n * hidden_dim * 2;
+    for (int32_t i0 = 0; i0 < nb; i0 += a8r::kBatch) {
+        a8r::StreamBatch sb;
+        fill_batch(c, layer, b0 + i0, std::min(a8r::kBatch, nb - i0), &sb);
+        hipError_t e = a8r::launch_rebuild(c->geo, layer, sb, n, hidden_dim, (const uint8_t*)hidden + i0 * row,
+                                           w_k, w_v, c->stream);
+        if (e != hipSuccess) return device_fail(c, e, "window rebuild kernel");
+    }
+    c->ledger.rebuild(layer, b0, nb, n);
     return ok();
 }
 

@@ -110,6 +110,12 @@ hipError_t launch_attention(const Geometry& g, int layer, const StreamBatch& now
 hipError_t launch_append_decode(const Geometry& g, int layer, const StreamBatch& before,
                                 const void* k, const void* v, const void* q, void* out,
                                 bool allow_mfma, int n_cu, hipStream_t s);
+// Window re-prefill: K = H Wk^T, V = H Wv^T for the n tokens of each stream's
+// window (H device [nb][n][hidden] bf16, Wk and Wv device [Hkv*D][hidden] bf16),
+// written to slots 0 .. n-1 of `layer`; the device state record becomes
+// (P, n, n mod W).  Needs bf16, hidden % 64 == 0 and Hkv*D % 128 == 0.
+hipError_t launch_rebuild(const Geometry& g, int layer, const StreamBatch& st, int n, int hidden, const void* h,
+                          const void* wk, const void* wv, hipStream_t s);
 // The device address of the library's static scratch array (kStaticScratchBytes,
 // 256-byte aligned) on `device`, looked up once per device and kept.
 hipError_t static_scratch(int device, void** ptr);

@@ -1886,6 +1886,170 @@ hipError_t run_chunk_pipe(const Geometry& g, int layer, const StreamBatch& st, i
     return launch_combine<D, 2>(g, st.nb, n_q, n_split, out, s);
 }
 
+// ------------------------------------------------------ window re-prefill ----
+// Rebuilds the window of a batch of streams from stored hidden states, the way
+// "audio8-asr-infinite-p150" (section "Limitations") rebuilds its rolling
+// context by re-prefilling instead of trimming: K = H Wk^T and V = H Wv^T for
+// the n tokens of each stream's window (H: [n][hidden], Wk, Wv: [Hkv*D][hidden],
+// the layout of a linear layer's weight), bf16 operands on
+// v_mfma_f32_16x16x32_bf16 with float32 accumulation, each result rounded once
+// to bf16 (nearest even).  Token j of the window goes to ring slot j: K rows as
+// appended, V into its transposed 8-slot block.
+//
+// One block of 4 waves per (128-token tile of one stream, 128 output columns);
+// the columns are K's Hkv*D then V's.  Waves take 64 x 64 quarters of the tile
+// (4 x 4 MFMA tiles each).  A and B (both k-contiguous) are staged through LDS
+// in 64-wide k steps, double-buffered, rows padded by 16 bytes so that the
+// operand reads of eight consecutive lanes (eight rows) fall on distinct banks.
+// The blocks of one token tile are 8 block ids apart, so they run on one XCD
+// and read the token tile from HBM once.  The epilogue stages the bf16 tile in
+// LDS and writes whole 16-byte chunks: K rows, or 8 consecutive slots of one
+// dim for V.  Tokens past n load as zeros; their V entries in the last 8-slot
+// block are written as zeros (those slots are not live).
+constexpr int kRbM = 128, kRbN = 128, kRbK = 64;
+constexpr int kRbRow = kRbK * 2 + 16;                  // LDS bytes per staged row (A or B)
+constexpr int kRbOut = kRbN * 2 + 16;                  // LDS bytes per epilogue row
+
+__global__ __launch_bounds__(256, 2) void rebuild_kernel(Geometry g, int layer, StreamBatch st, int n, int hidden,
+                                                         const uint16_t* __restrict__ h,
+                                                         const uint16_t* __restrict__ wk,
+                                                         const uint16_t* __restrict__ wv, int n_row_tiles,
+                                                         int n_col_tiles) {
+    __shared__ __align__(16) unsigned char lds[2 * 2 * kRbM * kRbRow];   // [buffer][A, B][128 rows]
+    static_assert(kRbM * kRbOut <= 2 * 2 * kRbM * kRbRow, "epilogue tile does not fit");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n16 = lane & 15, gq = lane >> 4;
+    // block id -> (stream, token tile, column tile): the column tiles of one
+    // token tile are 8 ids apart (one XCD)
+    const int id = blockIdx.x;
+    const int col_t = (id >> 3) % n_col_tiles;
+    const int tile = (id & 7) + 8 * ((id >> 3) / n_col_tiles);
+    if (tile >= st.nb * n_row_tiles) return;
+    const int bi = tile / n_row_tiles, row0 = (tile % n_row_tiles) * kRbM;
+    const int D = g.d, kvd = g.hkv * D, col0 = col_t * kRbN;
+    const bool is_v = col0 >= kvd;
+    const uint16_t* w = is_v ? wv + (int64_t)(col0 - kvd) * hidden : wk + (int64_t)col0 * hidden;
+    const uint16_t* hrow = h + (int64_t)bi * n * hidden;
+
+    // staging: each thread moves 4 chunks of 16 bytes of A and of B per k step
+    // (128 rows x 128 bytes each): row tid / 8 + 32 u, chunk tid % 8
+    const int sr = tid >> 3, sc = tid & 7;
+    u32x4 ra[4], rb[4];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = sr + 32 * u;
+            const int tok = row0 + r;
+            ra[u] = tok < n ? *(const u32x4*)(hrow + (int64_t)tok * hidden + k0 + 8 * sc) : u32x4{0u, 0u, 0u, 0u};
+            rb[u] = *(const u32x4*)(w + (int64_t)r * hidden + k0 + 8 * sc);
+        }
+    };
+    auto stage = [&](int buf) {
+        unsigned char* a = lds + buf * 2 * kRbM * kRbRow;
+        unsigned char* b = a + kRbM * kRbRow;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            *(u32x4*)(a + (sr + 32 * u) * kRbRow + 16 * sc) = ra[u];
+            *(u32x4*)(b + (sr + 32 * u) * kRbRow + 16 * sc) = rb[u];
+        }
+    };
+
+    // wave (wm, wn) computes rows 64 wm .., columns 64 wn ..
+    const int wm = wave >> 1, wn = wave & 1;
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int n_k = hidden / kRbK;
+    load(0);
+    stage(0);
+    __syncthreads();
+    for (int kt = 0; kt < n_k; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < n_k) load((kt + 1) * kRbK);          // next step's operands in flight
+        const unsigned char* a = lds + buf * 2 * kRbM * kRbRow;
+        const unsigned char* b = a + kRbM * kRbRow;
+#pragma unroll
+        for (int kb = 0; kb < kRbK / 32; ++kb) {
+            bf16x8 af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                af[i] = *(const bf16x8*)(a + (64 * wm + 16 * i + n16) * kRbRow + 2 * (32 * kb + 8 * gq));
+                bf[i] = *(const bf16x8*)(b + (64 * wn + 16 * i + n16) * kRbRow + 2 * (32 * kb + 8 * gq));
+            }
+            // C^T tile (i, j): rows = output columns (B), columns = tokens (A),
+            // so a lane holds 4 consecutive columns of one token
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < n_k) {
+            stage(buf ^ 1);        // the other buffer: last read in step kt - 1, before its barrier
+            __syncthreads();
+        }
+    }
+    __syncthreads();               // every wave is done with the operand buffers
+
+    // epilogue: bf16 tile [token][column] in LDS, then 16-byte global stores
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // acc[i][j][e]: column 64 wn + 16 j + 4 gq + e, token 64 wm + 16 i + n16
+            const int tok = 64 * wm + 16 * i + n16, col = 64 * wn + 16 * j + 4 * gq;
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = (__bf16)acc[i][j][e];
+            *(bf16x4*)(lds + tok * kRbOut + 2 * col) = v4;
+        }
+    __syncthreads();
+    const int b = st.b0 + bi;
+    if (!is_v) {
+        // 128 tokens x 16 chunks of 16 bytes (128 columns: one or two heads)
+        for (int t = tid; t < kRbM * (kRbN / 8); t += 256) {
+            const int tok = t >> 4, ch = t & 15;
+            if (row0 + tok >= n) continue;
+            const int col = col0 + 8 * ch, kh = col / D, d = col % D;
+            uint16_t* dst = (uint16_t*)g.k_ring + ((pair_index(g, layer, b, kh) * g.pair_slots + row0 + tok) * D + d);
+            *(u32x4*)dst = *(const u32x4*)(lds + tok * kRbOut + 16 * ch);
+        }
+    } else {
+        // 16 groups of 8 slots x 128 dims: 8 consecutive slots of one dim
+        for (int t = tid; t < (kRbM / 8) * kRbN; t += 256) {
+            const int grp = t / kRbN, c = t % kRbN;
+            if (row0 + 8 * grp >= n) continue;
+            const int col = col0 - kvd + c, kh = col / D, d = col % D;
+            u32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = *(const uint16_t*)(lds + (8 * grp + 2 * e) * kRbOut + 2 * c);
+                const uint32_t hi = *(const uint16_t*)(lds + (8 * grp + 2 * e + 1) * kRbOut + 2 * c);
+                v[e] = lo | (hi << 16);
+            }
+            const int slot0 = row0 + 8 * grp;
+            uint16_t* dst = (uint16_t*)g.v_ring +
+                            ((pair_index(g, layer, b, kh) * (g.pair_slots / 8) + slot0 / 8) * (int64_t)D + d) * 8;
+            *(u32x4*)dst = v;
+        }
+    }
+}
+
+// Device record of the rebuilt streams' state: (P, n, n mod W) in `layer`.
+__global__ void rebuild_state_kernel(Geometry g, int layer, StreamBatch st, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= st.nb) return;
+    DevState s;
+    s.next_pos = st.next_pos[i];
+    s.length = n;
+    s.next_slot = n == g.window ? 0 : n;
+    g.state[(int64_t)layer * g.n_streams + st.b0 + i] = s;
+}
+
 bool mfma_chunk_ok(const Geometry& g, int n_q) {
     return g.elem_bytes == 2 && (g.d == 64 || g.d == 128) && n_q >= 2 && n_q <= kMaxPartialQ;
 }
@@ -2016,6 +2180,20 @@ hipError_t launch_append_decode(const Geometry& g, int layer, const StreamBatch&
         now.next_slot[i] = now.next_slot[i] + 1 == g.window ? 0 : now.next_slot[i] + 1;
     }
     return launch_attention(g, layer, now, 1, q, out, allow_mfma, n_cu, s);
+}
+
+hipError_t launch_rebuild(const Geometry& g, int layer, const StreamBatch& st, int n, int hidden, const void* h,
+                          const void* wk, const void* wv, hipStream_t s) {
+    const int n_row_tiles = (n + kRbM - 1) / kRbM;
+    const int n_col_tiles = 2 * g.hkv * g.d / kRbN;
+    const int tiles = st.nb * n_row_tiles;
+    const int blocks = 8 * n_col_tiles * ((tiles + 7) / 8);
+    hipLaunchKernelGGL(rebuild_kernel, dim3(blocks), dim3(256), 0, s, g, layer, st, n, hidden, (const uint16_t*)h,
+                       (const uint16_t*)wk, (const uint16_t*)wv, n_row_tiles, n_col_tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(rebuild_state_kernel, dim3((st.nb + 127) / 128), dim3(128), 0, s, g, layer, st, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_append_chunk(const Geometry& g, int layer, const StreamBatch& before, int n, const void* k,

@@ -25,6 +25,10 @@ hipError_t launch_attention(const Geometry&, int, const StreamBatch&, int, const
     return hipErrorNoDevice;
 }
 hipError_t static_scratch(int, void**) { return hipErrorNoDevice; }
+hipError_t launch_rebuild(const Geometry&, int, const StreamBatch&, int, int, const void*, const void*, const void*,
+                          hipStream_t) {
+    return hipErrorNoDevice;
+}
 hipError_t launch_append_decode(const Geometry&, int, const StreamBatch&, const void*, const void*, const void*,
                                 void*, bool, int, hipStream_t) {
     return hipErrorNoDevice;
