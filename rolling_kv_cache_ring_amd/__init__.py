@@ -75,6 +75,15 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise LibraryNotBuilt(f"{LIB_PATH} not found: build it with "
                               "`python -m rolling_kv_cache_ring_amd.build`")
+    # PyTorch wheels for ROCm ship their own HIP runtime under the same soname
+    # as the system's; whichever is loaded first serves the whole process.
+    # Loading the library before PyTorch would bring in a second HIP/HSA
+    # runtime beside PyTorch's, and the second to open the GPU finds none, so
+    # PyTorch (when installed) is imported first.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     st = ctypes.c_int
     L.a8r_workspace_bytes.argtypes = [ctypes.POINTER(Config)]
