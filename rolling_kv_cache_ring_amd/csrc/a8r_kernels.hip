@@ -1400,7 +1400,11 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         const int rho = vs.rho;
         const unsigned char* row = (const unsigned char*)(c.table + (int64_t)(rho < 0 ? -rho : rho) * (D / 2));
         constexpr int q4 = PB::kC / 4;                  // bytes of the row per wave
-        if (lane < q4 / 16) dma16(row + wave * q4 + 16 * lane, slot + PB::kK + wave * q4);
+        if (lane < q4 / 16) {
+            // staged chunk p = 8 i + c holds chunk (P/2) c + i of the table row
+            const int p = wave * (q4 / 16) + lane;
+            dma16(row + 16 * ((P / 2) * (p & 7) + (p >> 3)), slot + PB::kK + wave * q4);
+        }
     };
     auto issue_v = [&](int v, unsigned char* slot) {
         const VisitSrc vs = visit_src(c, v < n_mine ? kvis(v) : 0);
@@ -1419,6 +1423,10 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     // first wait below is unconditional.
     const int kr_t = 8 * wave + (lane >> 3);           // key offset this lane rotates
     const int kr_i = P * (lane & 7);                   // its first pair index
+    // The staged R(rho) row: lane group c = lane & 7 needs the P/2 16-byte
+    // chunks (P/2) c + i of the table row; they are staged at 8 i + c, so the
+    // eight groups' reads of one i are consecutive chunks (no bank conflict)
+    // at compile-time offsets from the group's base.
     // R(kr_t) for those pairs, for the whole walk (table row kr_t < 32)
     float2 rt[P];
 #pragma unroll
@@ -1442,19 +1450,24 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     }
     // Fused append (one row group): the new tokens of this (stream, KV head)
     // whose tiles are among this block's visits are copied into their ring
-    // slots, as append_kernel writes them, and the block
-    // waits for the stores (and the query and table loads above, issued first
-    // so that their latency overlaps) before its first K/V load.  No other
-    // block reads those tiles in this call.
+    // slots, as append_kernel writes them.  No other block reads those tiles
+    // in this call.  The stores must be in the L2 before any wave loads one of
+    // those tiles.  When none of them is among the first loads issued below
+    // (visits k0 .. k0 + 2 WG - 1), the stores overlap those loads: step -1
+    // waits for everything (vmcnt 0) before its barrier, and every later load
+    // is issued after that barrier; otherwise the block waits for the stores
+    // here (and for the query and table loads above, issued first so that
+    // their latency overlaps) before its first K/V load.
     if (fused) {
         auto visit_of = [&](int slot) {
             const int v = slot / kTile - c.p0t;
             return v < 0 ? v + c.n_tiles : v;
         };
-        bool mine = false;                             // block-uniform
+        bool mine = false, early = false;               // block-uniform
         for (int j = 0; j < C; ++j) {
             const int v = visit_of(wrap_slot(s_prev + j, W));
             mine = mine || (v >= k0 && v < k1);
+            early = early || (v >= k0 && v < k1 && v < k0 + 2 * WG);
         }
         if (mine) {
             constexpr int chunks = D / 8;              // 16-byte chunks of a bf16 row
@@ -1468,8 +1481,10 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
                                          (const uint8_t*)v_new + src);
                 }
             }
-            __builtin_amdgcn_s_waitcnt(0);             // the tokens are in the L2 ...
-            __syncthreads();                           // ... before any wave loads a tile
+            if (early) {
+                __builtin_amdgcn_s_waitcnt(0);         // the tokens are in the L2 ...
+                __syncthreads();                       // ... before any wave loads a tile
+            }
         }
         if (kh == 0 && split == 0 && tid == 0) {      // record of the new state
             DevState ns;
@@ -1507,7 +1522,8 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     // newest, get R(W) on top), composed with the lane's R(kr_t).  The key is
     // rounded to bf16 once, as the MFMA operand.
     auto rotate = [&](const unsigned char* kslot, unsigned char* tile, bool first, bool seam) {
-        const float4* br = (const float4*)(kslot + PB::kK) + kr_i / 2;
+        const float4* brow = (const float4*)(kslot + PB::kK) + (lane & 7);
+        auto br = [&](int i2) { return brow[8 * i2]; };
         const unsigned char* kraw = kslot + kr_t * D * 2;
         uint32_t x1w[P / 2], x2w[P / 2];
         if constexpr (P == 8) {
@@ -1528,7 +1544,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         float2 cf[P];
 #pragma unroll
         for (int i2 = 0; i2 < P / 2; ++i2) {
-            const float4 b4 = br[i2];
+            const float4 b4 = br(i2);
             cf[2 * i2] = float2{b4.x, b4.y};
             cf[2 * i2 + 1] = float2{b4.z, b4.w};
         }
@@ -1537,7 +1553,7 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
             const float4* wr = (const float4*)lds_rw + kr_i / 2;
 #pragma unroll
             for (int i2 = 0; i2 < P / 2; ++i2) {
-                const float4 b4 = br[i2], w4 = wr[i2];
+                const float4 b4 = br(i2), w4 = wr[i2];
                 const float2 a2[2] = {float2{b4.x, -b4.y}, float2{b4.z, -b4.w}};
                 const float2 w2[2] = {float2{w4.x, w4.y}, float2{w4.z, w4.w}};
 #pragma unroll
@@ -1590,7 +1606,10 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     // (and everything issued before it) has landed once at most K(1) and V(0)
     // are outstanding.
     {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PB::nK + PB::nV));
+        // everything issued so far: K(0), and the new tokens' stores where
+        // they overlapped the first loads (unconditional, so that the
+        // compiler knows no store is pending inside the walk)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __builtin_amdgcn_s_barrier();                  // every wave's share
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
