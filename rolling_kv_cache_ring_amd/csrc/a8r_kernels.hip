@@ -543,10 +543,23 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 // the new token's tile writes the token into its ring slot before it reads that
 // tile (no other wave touches that slot).
 
+// A raw buffer resource over `bytes` bytes at `base`: buffer loads take a
+// 32-bit per-lane offset plus a scalar offset, and reads past the end return
+// zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) buffer, 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
 struct DecodeCtx {
     const uint16_t* kp;
     const uint16_t* vp;
     const float2* table;
+    rsrc_t kr, vr, tr;     // the pair's K and V blocks and the table, as buffers
+    uint32_t koff[8];      // this lane's byte offsets inside a tile's K rows, per load
+    uint32_t voff, toff;   // ... inside a tile's V blocks, and inside a table row
     int oldest, t_o, p0t, n_tiles, L, W, rq, tb0, tb1, gq, n;
     int n_roll, F;     // visits over the ring, then ceil(F / 32) over the prefix
     int pre_on;        // a pinned prefix may exist (compile-time in every kernel: without it
@@ -639,6 +652,17 @@ __device__ __forceinline__ lds_void* opaque_lds(unsigned char* p) {
     return (lds_void*)(size_t)off;
 }
 
+// The same from an LDS address already converted (lds_u32): the conversion
+// of a generic pointer to an LDS address tests it for null, a 64-bit scalar
+// compare and select per load when done for every load.
+__device__ __forceinline__ uint32_t lds_u32(unsigned char* p) { return (uint32_t)(size_t)(lds_void*)p; }
+
+__device__ __forceinline__ lds_void* opaque_lds(uint32_t a) {
+    unsigned off = __builtin_amdgcn_readfirstlane(a);
+    asm volatile("" : "+s"(off));
+    return (lds_void*)(size_t)off;
+}
+
 // Compiler-level memory barrier (no instruction): loads and stores do not move
 // across it.
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
@@ -659,6 +683,16 @@ template <bool STREAM>
 __device__ __forceinline__ void dma16_policy(const void* src, unsigned char* lds_dst) {
     constexpr int kNonTemporal = 2;   // cache-policy bit NT of the load
     __builtin_amdgcn_global_load_lds(src, opaque_lds(lds_dst), 16, 0, STREAM ? kNonTemporal : 0);
+}
+
+// The decode walk's global->LDS loads go through buffer resources (make_rsrc):
+// a lane's offsets inside a tile are computed once and each visit adds only
+// its tile's scalar byte offset (a global load needs a 64-bit per-lane address
+// computed for every load).
+template <bool STREAM>
+__device__ __forceinline__ void bdma16(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds_dst) {
+    constexpr int kNonTemporal = 2;   // cache-policy bit NT of the load
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, opaque_lds(lds_dst), 16, voff, soff, 0, STREAM ? kNonTemporal : 0);
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
@@ -698,26 +732,39 @@ __device__ __forceinline__ void dma_table_row(const float2* table, int row, int 
 // The coefficient row staged after the K rows: R(r_q - rho), the query's
 // rotation for this visit (R(r_q) when the keys are stored rotated to their
 // index).
-template <int D, bool STREAM>
-__device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, unsigned char* kbuf) {
+// The lane's fixed offsets of the decode walk's buffer loads (dec_load_k /
+// dec_load_v): K row r = RPI j + lane / (D/8) of a tile, its swizzled
+// 16-byte column, for load j; the 8 slots of V dim n of the tile's 8-slot
+// block gq; 16 bytes of a table row (lanes past the row re-read its end).
+template <int D>
+__device__ __forceinline__ void dec_lane_offsets(DecodeCtx& c, int lane) {
     constexpr int RPI = 64 / (D / 8);            // rows per instruction
-    const VisitSrc vs = visit_src(c, k);
     const int rl = lane / (D / 8), sl = lane % (D / 8);
 #pragma unroll
     for (int j = 0; j < 2 * (D / 32); ++j) {
         const int r = RPI * j + rl;
         const int col = 8 * (sl >> 3) + ((sl & 7) ^ k_swz(r));
-        dma16_policy<STREAM>(c.kp + (int64_t)(vs.tile * kTile + r) * D + 8 * col, kbuf + j * 1024);
+        c.koff[j] = (uint32_t)((r * D + 8 * col) * 2);
     }
-    dma_table_row<D>(c.table, c.rq - (c.prerot ? 0 : vs.rho), lane, kbuf + 2 * (D / 32) * 1024);
+    c.voff = (uint32_t)(((c.gq * D + c.n) * 8) * 2);
+    c.toff = (uint32_t)(16 * lane < 4 * D ? 16 * lane : 4 * D - 16);
 }
 
 template <int D, bool STREAM>
-__device__ __forceinline__ void dec_load_v(const DecodeCtx& c, int k, unsigned char* vbuf) {
+__device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, uint32_t kbuf) {
     const VisitSrc vs = visit_src(c, k);
-    const uint16_t* vb = c.vp + ((int64_t)(vs.tile * 4 + c.gq) * D + c.n) * 8;
+    const uint32_t tile_off = (uint32_t)vs.tile * (kTile * D * 2);
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) dma16_policy<STREAM>(vb + (int64_t)nb * 16 * 8, vbuf + nb * 1024);
+    for (int j = 0; j < 2 * (D / 32); ++j) bdma16<STREAM>(c.kr, c.koff[j], tile_off, kbuf + j * 1024);
+    bdma16<false>(c.tr, c.toff, (uint32_t)(c.rq - (c.prerot ? 0 : vs.rho)) * (D * 4), kbuf + 2 * (D / 32) * 1024);
+}
+
+template <int D, bool STREAM>
+__device__ __forceinline__ void dec_load_v(const DecodeCtx& c, int k, uint32_t vbuf) {
+    const VisitSrc vs = visit_src(c, k);
+    const uint32_t tile_off = (uint32_t)vs.tile * (kTile * D * 2);
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) bdma16<STREAM>(c.vr, c.voff, tile_off + nb * 256, vbuf + nb * 1024);
 }
 
 // A visit's K part copied from LDS into registers: the query-rotation pairs
@@ -943,6 +990,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     unsigned char* va = lds_va + wave * B::kV;
     unsigned char* kb = lds_kb + wave * B::kK;
     unsigned char* vb = lds_vb + wave * B::kV;
+    const uint32_t ka_u = lds_u32(ka), va_u = lds_u32(va), kb_u = lds_u32(kb), vb_u = lds_u32(vb);
 
     // window after the (optional) append of one token
     const int s_prev = st.next_slot[bi];
@@ -967,6 +1015,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     const int64_t pair = pair_index(g, layer, b, kh);
     c.kp = (const uint16_t*)g.k_ring + pair * g.pair_slots * D;
     c.vp = (const uint16_t*)g.v_ring + pair * g.pair_slots * D;
+    c.kr = make_rsrc(c.kp, (uint32_t)g.pair_slots * D * 2);
+    c.vr = make_rsrc(c.vp, (uint32_t)g.pair_slots * D * 2);
+    c.tr = make_rsrc(g.table, (uint32_t)(g.window + g.f_pad + kTablePad) * D * 4);
+    dec_lane_offsets<D>(c, lane);
     int n_visit;
     {
         int last = c.oldest + L - 1;
@@ -1037,14 +1089,14 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     // then K(k), V(k), K(k + 4), V(k + 4) of the wave's first two visits (those
     // that exist), and a wait for everything up to K(k)
     if (k + 4 < k1) {
-        dec_load_k<D, STREAM>(c, k, lane, ka);
-        dec_load_v<D, STREAM>(c, k, va);
-        dec_load_k<D, STREAM>(c, k + 4, lane, kb);
-        dec_load_v<D, STREAM>(c, k + 4, vb);
+        dec_load_k<D, STREAM>(c, k, lane, ka_u);
+        dec_load_v<D, STREAM>(c, k, va_u);
+        dec_load_k<D, STREAM>(c, k + 4, lane, kb_u);
+        dec_load_v<D, STREAM>(c, k + 4, vb_u);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV + B::nK + B::nV));
     } else if (k < k1) {
-        dec_load_k<D, STREAM>(c, k, lane, ka);
-        dec_load_v<D, STREAM>(c, k, va);
+        dec_load_k<D, STREAM>(c, k, lane, ka_u);
+        dec_load_v<D, STREAM>(c, k, va_u);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
     } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1092,13 +1144,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         if (k == k_tok) patch_k<D>(ka, t_tok, lane, ((const u32x4*)lds_tok)[lane & (D / 8 - 1)]);
         dec_read_k<D>(c, ka, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);                                 // copied out of ka
-        if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, ka);
+        if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, ka_u);
         bf16x8 pb = dec_scores<D, true>(c, k, rk, kcr, qraw, lds_rw, o, m, l);
         wait_v(k);
         if (k == k_tok) patch_v<D>(va, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(va, lane, rv);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_v<D, STREAM>(c, k + 8, va);
+        if (k + 8 < k1) dec_load_v<D, STREAM>(c, k + 8, va_u);
         dec_pv<D>(rv, pb, o);
         k += 4;
         if (k >= k1) break;
@@ -1106,13 +1158,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         if (k == k_tok) patch_k<D>(kb, t_tok, lane, ((const u32x4*)lds_tok)[lane & (D / 8 - 1)]);
         dec_read_k<D>(c, kb, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, kb);
+        if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, kb_u);
         pb = dec_scores<D, false>(c, k, rk, kcr, qraw, lds_rw, o, m, l);
         wait_v(k);
         if (k == k_tok) patch_v<D>(vb, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(vb, lane, rv);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_v<D, STREAM>(c, k + 8, vb);
+        if (k + 8 < k1) dec_load_v<D, STREAM>(c, k + 8, vb_u);
         dec_pv<D>(rv, pb, o);
         k += 4;
     }
@@ -1853,7 +1905,11 @@ bool any_prefix(const StreamBatch& st) {
 }
 
 bool mfma_decode_ok(const Geometry& g) {
-    return g.elem_bytes == 2 && g.group <= 16 && (g.d == 64 || g.d == 128);
+    // the walk's buffer offsets are 32-bit: a pair's K (or V) block and the
+    // table stay below 2 GiB (windows up to 8M tokens at D = 128)
+    return g.elem_bytes == 2 && g.group <= 16 && (g.d == 64 || g.d == 128) &&
+           (int64_t)g.pair_slots * g.d * 2 < ((int64_t)1 << 31) &&
+           (int64_t)(g.window + g.f_pad + kTablePad) * g.d * 4 < ((int64_t)1 << 31);
 }
 
 template <int D, int EB>
