@@ -1413,6 +1413,9 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     const int64_t pair = pair_index(g, layer, b, kh);
     c.kp = (const uint16_t*)g.k_ring + pair * g.pair_slots * D;
     c.vp = (const uint16_t*)g.v_ring + pair * g.pair_slots * D;
+    c.kr = make_rsrc(c.kp, (uint32_t)g.pair_slots * D * 2);
+    c.vr = make_rsrc(c.vp, (uint32_t)g.pair_slots * D * 2);
+    c.tr = make_rsrc(g.table, (uint32_t)(g.window + g.f_pad + kTablePad) * D * 4);
     int n_visit;
     {
         int last = c.oldest + L - 1;
@@ -1440,31 +1443,35 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
     // R(rho) row, |rho| for the first visit) and of its V part
     // (a v past the group's visits loads the pair's first tile instead, which
     // is always in range; its slot is never read)
-    auto issue_k = [&](int v, unsigned char* slot) {
+    // (buffer loads: the lane's offset inside a tile is fixed, the tile's
+    // offset is scalar; LDS slots as 32-bit addresses, converted once)
+    const uint32_t ring_k_u = lds_u32(ring_k), ring_v_u = lds_u32(ring_v);
+    const uint32_t k_lane = 16 * lane;
+    constexpr int q4 = PB::kC / 4;                      // bytes of the R(rho) row per wave
+    // staged chunk p = 8 i + c of the R(rho) row holds chunk (P/2) c + i of the table row
+    const int row_p = wave * (q4 / 16) + (lane & (q4 / 16 - 1));
+    const uint32_t row_lane = 16 * ((P / 2) * (row_p & 7) + (row_p >> 3));
+    const uint32_t v_lane = (uint32_t)((gq * D + n) * 16);
+    auto issue_k = [&](int v, uint32_t slot) {
         const int kv = v < n_mine ? kvis(v) : 0;
         const VisitSrc vs = visit_src(c, kv);
-        const unsigned char* krow = (const unsigned char*)(c.kp + (int64_t)vs.tile * kTile * D);
+        const uint32_t tile_off = (uint32_t)vs.tile * (kTile * D * 2);
 #pragma unroll
         for (int u = 0; u < PB::nK - 1; ++u) {
             const int j = wave * (PB::nK - 1) + u;
-            dma16(krow + j * 1024 + 16 * lane, slot + j * 1024);
+            bdma16<false>(c.kr, k_lane, tile_off + j * 1024, slot + j * 1024);
         }
         const int rho = vs.rho;
-        const unsigned char* row = (const unsigned char*)(c.table + (int64_t)(rho < 0 ? -rho : rho) * (D / 2));
-        constexpr int q4 = PB::kC / 4;                  // bytes of the row per wave
-        if (lane < q4 / 16) {
-            // staged chunk p = 8 i + c holds chunk (P/2) c + i of the table row
-            const int p = wave * (q4 / 16) + lane;
-            dma16(row + 16 * ((P / 2) * (p & 7) + (p >> 3)), slot + PB::kK + wave * q4);
-        }
+        if (lane < q4 / 16)
+            bdma16<false>(c.tr, row_lane, (uint32_t)(rho < 0 ? -rho : rho) * (D * 4), slot + PB::kK + wave * q4);
     };
-    auto issue_v = [&](int v, unsigned char* slot) {
+    auto issue_v = [&](int v, uint32_t slot) {
         const VisitSrc vs = visit_src(c, v < n_mine ? kvis(v) : 0);
-        const uint16_t* vb = c.vp + ((int64_t)(vs.tile * 4 + gq) * D + n) * 8;
+        const uint32_t tile_off = (uint32_t)vs.tile * (kTile * D * 2);
 #pragma unroll
         for (int u = 0; u < PB::nV; ++u) {
             const int nb = wave * PB::nV + u;
-            dma16(vb + (int64_t)nb * 16 * 8, slot + nb * 1024);
+            bdma16<false>(c.vr, v_lane, tile_off + nb * 256, slot + nb * 1024);
         }
     };
 
@@ -1547,9 +1554,9 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         }
     }
 
-    issue_k(0, ring_k);
-    issue_k(1, ring_k + PB::kKC);
-    issue_v(0, ring_v);
+    issue_k(0, ring_k_u);
+    issue_k(1, ring_k_u + PB::kKC);
+    issue_v(0, ring_v_u);
 
     // column blocks with at least one real row (wave-uniform)
     const bool act0 = row0 + 16 * wave < rows, act1 = NW > 1 && row0 + 16 * (wave + 4) < rows;
@@ -1665,8 +1672,8 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         __builtin_amdgcn_s_barrier();                  // every wave's share
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
-        if (n_mine > 2) issue_k(2, ring_k + 2 * PB::kKC);
-        if (n_mine > 1) issue_v(1, ring_v + PB::kV);
+        if (n_mine > 2) issue_k(2, ring_k_u + 2 * PB::kKC);
+        if (n_mine > 1) issue_v(1, ring_v_u + PB::kV);
         if (n_mine > 0) {
             // the first visit of the ring (rho = -t_o) and prefix visits (rho < 0)
             // compose R(rho) from the conjugate of row |rho|
@@ -1720,8 +1727,8 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
-        if (s + 3 < n_mine) issue_k(s + 3, ring_k + (S % 3) * PB::kKC);
-        if (s + 2 < n_mine) issue_v(s + 2, ring_v + ((S + 2) % 3) * PB::kV);
+        if (s + 3 < n_mine) issue_k(s + 3, ring_k_u + (S % 3) * PB::kKC);
+        if (s + 2 < n_mine) issue_v(s + 2, ring_v_u + ((S + 2) % 3) * PB::kV);
 
         const int kv = kvis(s);
         const VisitSrc vs = visit_src(c, kv);
@@ -2126,7 +2133,10 @@ __global__ void rebuild_state_kernel(Geometry g, int layer, StreamBatch st, int 
 }
 
 bool mfma_chunk_ok(const Geometry& g, int n_q) {
-    return g.elem_bytes == 2 && (g.d == 64 || g.d == 128) && n_q >= 2 && n_q <= kMaxPartialQ;
+    // 32-bit buffer offsets, as for the decode walk
+    return g.elem_bytes == 2 && (g.d == 64 || g.d == 128) && n_q >= 2 && n_q <= kMaxPartialQ &&
+           (int64_t)g.pair_slots * g.d * 2 < ((int64_t)1 << 31) &&
+           (int64_t)(g.window + g.f_pad + kTablePad) * g.d * 4 < ((int64_t)1 << 31);
 }
 
 }  // namespace
