@@ -298,7 +298,7 @@ __device__ __forceinline__ int64_t part_row(const Geometry& g, int bi, int kh, i
 // Merges the splits' partials: 256 threads, each 4 consecutive dims of one
 // output row (stream, query, head); D/4 threads per row.  Every split's loads
 // are issued together (one round trip), then combined in split order.
-template <int D, int EB>
+template <int D, int EB, int NS>
 __global__ __launch_bounds__(256) void combine_kernel(Geometry g, int n_q, int n_split, void* out, int rows) {
     constexpr int TPR = D / 4, RPB = 256 / TPR;          // threads per row, rows per block
     const int o = blockIdx.x * RPB + threadIdx.x / TPR;
@@ -308,34 +308,36 @@ __global__ __launch_bounds__(256) void combine_kernel(Geometry g, int n_q, int n
     const int c = (o / g.hq) % n_q;
     const int bi = o / (g.hq * n_q);
     const int kh = h / g.group, row = c * g.group + (h - kh * g.group);
-    float mv[kMaxSplits], lv[kMaxSplits];
-    float4 ov[kMaxSplits];
+    // Every load unconditional (a split past n_split re-reads the last one and
+    // gets weight 0) and at most NS (8 or 16) splits, so that they can all be
+    // in flight at once (with a branch per split the compiler waited for each
+    // split's loads before issuing the next).  The splits are merged online in
+    // split order, each split's m, l and O used together, so no load is held
+    // back behind arithmetic on the others.
+    float mv[NS], lv[NS];
+    float4 ov[NS];
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        if (s < n_split) {
-            const int64_t pr = part_row(g, bi, kh, s, row);
-            const float2 ml = *(const float2*)&g.part_ml[pr * 2];
-            mv[s] = ml.x;
-            lv[s] = ml.y;
-            ov[s] = *(const float4*)&g.part_o[pr * D + 4 * d4];
-        }
+    for (int s = 0; s < NS; ++s) {
+        const int64_t pr = part_row(g, bi, kh, s < n_split ? s : n_split - 1, row);
+        const float2 ml = *(const float2*)&g.part_ml[pr * 2];
+        mv[s] = ml.x;
+        lv[s] = ml.y;
+        ov[s] = *(const float4*)&g.part_o[pr * D + 4 * d4];
     }
-    float mmax = kNegBig;
+    __builtin_amdgcn_sched_barrier(0);                 // every load issued before the merge
+    float mmax = mv[0], den = lv[0];
+    float4 num = ov[0];
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
-        if (s < n_split) mmax = fmaxf(mmax, mv[s]);
-    float den = 0.f;
-    float4 num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-        if (s < n_split) {
-            const float w = exp2f(mv[s] - mmax);
-            den += w * lv[s];
-            num.x += w * ov[s].x;
-            num.y += w * ov[s].y;
-            num.z += w * ov[s].z;
-            num.w += w * ov[s].w;
-        }
+    for (int s = 1; s < NS; ++s) {
+        const bool live = s < n_split;                 // branch-free: past n_split a no-op
+        const float mn = live ? fmaxf(mmax, mv[s]) : mmax;
+        const float a = exp2f(mmax - mn), w = live ? exp2f(mv[s] - mn) : 0.f;
+        den = den * a + lv[s] * w;
+        num.x = num.x * a + ov[s].x * w;
+        num.y = num.y * a + ov[s].y * w;
+        num.z = num.z * a + ov[s].z * w;
+        num.w = num.w * a + ov[s].w * w;
+        mmax = mn;
     }
     const int64_t ob = (((int64_t)bi * n_q + c) * g.hq + h) * D + 4 * d4;
     store_elem<EB>(out, ob, num.x / den);
@@ -348,8 +350,8 @@ template <int D, int EB>
 hipError_t launch_combine(const Geometry& g, int nb, int n_q, int n_split, void* out, hipStream_t s) {
     constexpr int RPB = 256 / (D / 4);
     const int rows = nb * n_q * g.hq;
-    hipLaunchKernelGGL((combine_kernel<D, EB>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, g, n_q, n_split,
-                       out, rows);
+    auto kern = n_split <= 8 ? combine_kernel<D, EB, 8> : combine_kernel<D, EB, kMaxSplits>;
+    hipLaunchKernelGGL(kern, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, g, n_q, n_split, out, rows);
     return hipGetLastError();
 }
 
