@@ -494,7 +494,7 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 }
 
 // ------------------------------------------------------------ MFMA decode ----
-// bf16 decode for one (stream, KV head, split) per block of 4 waves.
+// bf16 decode for one (stream, KV head, split) per block of 8 waves.
 //
 // The ring is walked in physical 32-slot tiles ("visits"), starting with the
 // tile that holds the oldest live slot.  A visit's keys sit at slots s0 + t,
@@ -506,9 +506,9 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 // <R(r_q) q, R(rho + t) k> = <R(r_q - rho) q, R(t) k> because rotations in each
 // 2-D plane compose additively and are orthogonal.  The ring holds the keys as
 // appended; a lane always reads the same two offsets t of a tile (its MFMA
-// rows), so it keeps R(t) of those two rows in registers for the whole walk
-// and rotates its key rows by them on every visit (float32, one rounding to
-// the bf16 MFMA operand), while the query is rotated once per visit by
+// rows): the block stages the table rows R(t), t < 32, in LDS once, and each
+// lane rotates its two key rows by theirs on every visit (float32, one
+// rounding to the bf16 MFMA operand), while the query is rotated once per visit by
 // R(r_q - rho), a table row (< W + 32) fetched with the visit's keys.  On the
 // first visit the newest keys (offsets before the oldest slot, index
 // rho + t + W) take a second query rotation R(r_q - rho - W), composed in
@@ -526,13 +526,15 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 //
 // Memory pipeline: every global read of the kernel is a direct global->LDS
 // load (global_load_lds_dwordx4, 16 bytes per lane at LDS base + 16*lane), so
-// data in flight holds no registers.  Each wave owns two visit buffers, each
-// split in a K part (32 rows, whole cache lines per instruction, XOR-swizzled
-// for conflict-free MFMA operand reads, plus the visit's query-rotation row)
-// and a V part.  Order of issue: K(k), V(k), K(k+4), V(k+4); the scores of
-// visit k wait only for K(k), its PV only for V(k), and each part is refilled
-// with the visit two ahead as soon as it has been read, so about three
-// quarters of the wave's LDS are in flight at any time.  The waits are explicit
+// data in flight holds no registers.  Each wave owns one visit buffer, split
+// in a K part (32 rows, whole cache lines per instruction, XOR-swizzled for
+// conflict-free MFMA operand reads, plus the visit's query-rotation row) and a
+// V part.  The scores of visit k wait only for K(k), its PV only for V(k), and
+// each part is refilled with the wave's next visit (k + 8) as soon as it has
+// been read.  Two waves share each SIMD, so one wave's rotation, MFMA and
+// softmax work runs while the other waits for its loads (with one wave per
+// SIMD and two buffers each, the key rotation could not hide behind the
+// loads: 19.3 against 11.9 us for one 3B stream's layer).  The waits are explicit
 // vmcnt counts; the DMA destinations are hidden from the compiler's own wait
 // insertion (see opaque_lds), which would otherwise drain the queue.
 //
@@ -542,8 +544,9 @@ __global__ __launch_bounds__(256) void attn_portable(Geometry g, int layer, Stre
 //
 // Fused append: with k_new != nullptr the state in the arguments is the state
 // before the append, the window is the one after it, and the wave that owns
-// the new token's tile writes the token into its ring slot before it reads that
-// tile (no other wave touches that slot).
+// the new token's tile patches the token into its LDS copy of that tile and
+// writes it into its ring slot after the walk (no other wave or block reads
+// that slot in the same launch).
 
 // A raw buffer resource over `bytes` bytes at `base`: buffer loads take a
 // 32-bit per-lane offset plus a scalar offset, and reads past the end return
@@ -616,6 +619,22 @@ __device__ __forceinline__ void lds_coef(const unsigned char* row, int gq, float
     for (int kk = 0; kk < D / 64; ++kk)
 #pragma unroll
         for (int j = 0; j < 4; ++j) cf[kk][j] = p[16 * kk + j];
+}
+
+// The same from the block's copy of table rows 0 .. 31 (R(t) for a tile's key
+// t), row t's 16-byte chunk col at chunk position (D/4) t + (col ^ k_swz(t)):
+// the eight rows t of one read instruction's consecutive lanes then fall on
+// distinct banks.
+__device__ __forceinline__ int k_swz(int r);
+
+template <int D>
+__device__ __forceinline__ void lds_coef_t(const unsigned char* rows, int t, int gq, float4 (&cf)[D / 64][4]) {
+    const float4* p = (const float4*)rows + (D / 4) * t;
+    const int sw = k_swz(t);
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cf[kk][j] = p[(4 * gq + 16 * kk + j) ^ sw];
 }
 
 // Rotates a lane's slice of a bf16 row (dims 8*gq + 32*kk + e) by the pairs in
@@ -702,6 +721,10 @@ __device__ __forceinline__ void bdma16(rsrc_t r, uint32_t voff, uint32_t soff, u
 // "no LDS operation outstanding".
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// Waves per decode block: one visit buffer each, two waves per SIMD, so one
+// wave's rotation and MFMA work overlaps the other's loads.
+constexpr int kDecWaves = 8;
 
 // K part of a visit buffer: chunk (row r, 16-byte column col) of the 32 x D
 // tile at chunk position (D/8) r + 8 (col / 8) + ((col % 8) ^ swz(r)).  Each
@@ -794,11 +817,11 @@ __device__ __forceinline__ void dec_read_k(const DecodeCtx& c, const unsigned ch
 // Scores of visit k from its K part and the online-softmax update; returns
 // this lane's eight probabilities (keys 8*gq .. 8*gq+7, head n) as bf16.
 // SEAM: k may be the ring's first visit (only a wave's first visit can be).
-// kcr: R(tb0) and R(tb1) for the lane's pairs (table rows tb0, tb1; unused
+// lds_kc: the table rows R(t), t < 32, staged swizzled (lds_coef_t; unused
 // when the keys are stored rotated to their index).
 template <int D, bool SEAM>
 __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const DecK<D>& r,
-                                             const float4 (&kcr)[2][D / 64][4],
+                                             const unsigned char* lds_kc,
                                              const u32x4 (&qraw)[D / 32], const unsigned char* lds_rw,
                                              floatx4 (&o)[D / 16], float& m, float& l) {
     constexpr int KK = D / 32, NB = D / 16;
@@ -808,8 +831,11 @@ __device__ __forceinline__ bf16x8 dec_scores(const DecodeCtx& c, int k, const De
     rotate_row<D>(r.qc, qraw, qb);            // query by R(r_q - rho)
     bf16x8 ka[KK], kb[KK];                    // key rows tb0, tb1 by R(tb0), R(tb1)
     if (!c.prerot) {
-        rotate_row<D>(kcr[0], r.k0, ka);
-        rotate_row<D>(kcr[1], r.k1, kb);
+        float4 cf[D / 64][4];
+        lds_coef_t<D>(lds_kc, c.tb0, c.gq, cf);
+        rotate_row<D>(cf, r.k0, ka);
+        lds_coef_t<D>(lds_kc, c.tb1, c.gq, cf);
+        rotate_row<D>(cf, r.k1, kb);
     } else {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -959,28 +985,27 @@ __device__ __forceinline__ uint64_t merge_partials(uint64_t a, uint64_t b) {
 }
 
 template <int D, bool PREROT, bool PRE, bool STREAM>
-__global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, StreamBatch st,
-                                                      const uint16_t* __restrict__ q,
-                                                      uint16_t* __restrict__ out, int n_split,
-                                                      const uint16_t* __restrict__ k_new,
-                                                      const uint16_t* __restrict__ v_new) {
-    constexpr int KK = D / 32, NB = D / 16;
+__global__ __launch_bounds__(64 * kDecWaves, 1) void decode_mfma(Geometry g, int layer, StreamBatch st,
+                                                                const uint16_t* __restrict__ q,
+                                                                uint16_t* __restrict__ out, int n_split,
+                                                                const uint16_t* __restrict__ k_new,
+                                                                const uint16_t* __restrict__ v_new) {
+    constexpr int KK = D / 32, NB = D / 16, NWV = kDecWaves;
     using B = DecBuf<D>;
-    // per wave: buffer a and b, each a K part and a V part, four distinct LDS
-    // objects; then the block's query rows, R(W) row and new token
-    __shared__ __align__(16) unsigned char lds_ka[4 * B::kK];
-    __shared__ __align__(16) unsigned char lds_va[4 * B::kV];
-    __shared__ __align__(16) unsigned char lds_kb[4 * B::kK];
-    __shared__ __align__(16) unsigned char lds_vb[4 * B::kV];
+    // per wave one visit buffer, a K part and a V part (two LDS objects); then
+    // the block's query rows, R(W) row, new token and the R(t) rows t < 32
+    __shared__ __align__(16) unsigned char lds_k[NWV * B::kK];
+    __shared__ __align__(16) unsigned char lds_v[NWV * B::kV];
     __shared__ __align__(16) unsigned char lds_q[4096];
     __shared__ __align__(16) unsigned char lds_rw[1024];
     __shared__ __align__(16) unsigned char lds_tok[1024];
-    __shared__ float red_ml[4][16][2];
+    __shared__ __align__(16) unsigned char lds_kc[kTile * D * 4];
+    __shared__ float red_ml[NWV][16][2];
     // rows padded by 4 floats: the float4 writes of a column group's 16 lanes
     // (one row each) then spread over the banks
     constexpr int kRow = D + 4;
-    static_assert(4 * 16 * kRow * 4 <= 4 * B::kK, "merge buffer does not fit");
-    float (*red_o)[16][kRow] = (float (*)[16][kRow])lds_ka;   // after the walk
+    static_assert(NWV * 16 * kRow * 4 <= NWV * B::kK, "merge buffer does not fit");
+    float (*red_o)[16][kRow] = (float (*)[16][kRow])lds_k;   // after the walk
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -988,11 +1013,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     const int bi = blockIdx.z, kh = blockIdx.y, split = blockIdx.x;
     const int b = st.b0 + bi, G = g.group, W = g.window;
     const bool fused = k_new != nullptr;
-    unsigned char* ka = lds_ka + wave * B::kK;
-    unsigned char* va = lds_va + wave * B::kV;
-    unsigned char* kb = lds_kb + wave * B::kK;
-    unsigned char* vb = lds_vb + wave * B::kV;
-    const uint32_t ka_u = lds_u32(ka), va_u = lds_u32(va), kb_u = lds_u32(kb), vb_u = lds_u32(vb);
+    unsigned char* ka = lds_k + wave * B::kK;
+    unsigned char* va = lds_v + wave * B::kV;
+    const uint32_t ka_u = lds_u32(ka), va_u = lds_u32(va);
 
     // window after the (optional) append of one token
     const int s_prev = st.next_slot[bi];
@@ -1039,19 +1062,20 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     const int per = (n_visit + n_split - 1) / n_split;
     const int k0 = split * per, k1 = min(n_visit, k0 + per);
 
-    // R(tb0), R(tb1) for this lane's pairs (table rows < 32, L2-resident),
-    // kept in registers for the whole walk (staging them in LDS and reading
-    // them per visit was 0.6 us per launch slower at the 64-stream 3B shape);
-    // the oldest loads of the kernel, so every explicit wait below covers them
-    float4 kcr[2][D / 64][4];
+    // Table rows 0 .. 31 (R(t), t < 32) into lds_kc, swizzled (see
+    // lds_coef_t), an equal share per wave; the oldest loads of the kernel, so
+    // the prologue's wait covers them
     if (!PREROT) {
+        constexpr int kChunks = D / 4;                  // 16-byte chunks per row
+        constexpr int kInstr = kTile * kChunks / 64;    // loads for 32 rows
+        static_assert(kInstr % NWV == 0, "table rows are not split evenly");
+        const uint32_t kc_u = lds_u32(lds_kc);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float4* row = (const float4*)(g.table + (int64_t)(h ? c.tb1 : c.tb0) * (D / 2)) + 4 * gq;
-#pragma unroll
-            for (int kk = 0; kk < D / 64; ++kk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) kcr[h][kk][j] = row[16 * kk + j];
+        for (int u = 0; u < kInstr / NWV; ++u) {
+            const int j = wave * (kInstr / NWV) + u;
+            const int p = j * 64 + lane;                 // destination chunk
+            const int row = p / kChunks, col = p % kChunks;
+            bdma16<false>(c.tr, (uint32_t)(16 * (col ^ k_swz(row))), (uint32_t)row * (D * 4), kc_u + 1024 * j);
         }
     }
 
@@ -1065,7 +1089,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     if (fused) {
         int kv = s_prev / kTile - c.p0t;
         if (kv < 0) kv += c.n_tiles;
-        if (kv >= k0 && kv < k1 && (kv - k0) % 4 == wave) {
+        if (kv >= k0 && kv < k1 && (kv - k0) % NWV == wave) {
             // at most one wave per block: the token's K row to lds_tok[0, 2D),
             // its V row to [2D, 4D) (other lanes re-read the K row's start)
             k_tok = kv;
@@ -1078,25 +1102,19 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     }
 
     // Prologue, every load a direct global->LDS load (so the explicit wait
-    // counts are exact): a quarter of the query block (clamped to it), the
-    // R(W) row (wave 0), ...
+    // counts are exact): a quarter of the query block each for waves 0 .. 3
+    // (clamped to it), the R(W) row (wave 0), ...
     int k = k0 + wave;
     {
         const int qbytes = G * D * 2;
         int qo = wave * 1024 + 16 * lane;
         qo = qo < qbytes ? qo : qbytes - 16;
-        dma16((const unsigned char*)(q + ((int64_t)bi * g.hq + kh * G) * D) + qo, lds_q + wave * 1024);
+        if (wave < 4) dma16((const unsigned char*)(q + ((int64_t)bi * g.hq + kh * G) * D) + qo, lds_q + wave * 1024);
         if (wave == 0) dma_table_row<D>(g.table, W, lane, lds_rw);
     }
-    // then K(k), V(k), K(k + 4), V(k + 4) of the wave's first two visits (those
-    // that exist), and a wait for everything up to K(k)
-    if (k + 4 < k1) {
-        dec_load_k<D, STREAM>(c, k, lane, ka_u);
-        dec_load_v<D, STREAM>(c, k, va_u);
-        dec_load_k<D, STREAM>(c, k + 4, lane, kb_u);
-        dec_load_v<D, STREAM>(c, k + 4, vb_u);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV + B::nK + B::nV));
-    } else if (k < k1) {
+    // then K(k) and V(k) of the wave's first visit (if it exists), and a wait
+    // for everything up to K(k)
+    if (k < k1) {
         dec_load_k<D, STREAM>(c, k, lane, ka_u);
         dec_load_v<D, STREAM>(c, k, va_u);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
@@ -1119,56 +1137,42 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     for (int i = 0; i < NB; ++i) o[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m = kNegBig, l = 0.f;
 
-    // Visits k0 + wave, +4, ... alternate between buffers a and b.  Per visit:
-    // wait for its K part, copy it to registers, refill the buffer with the
-    // visit two ahead (if there is one), compute the scores; then the same for
-    // the V part and PV.  The loads in flight after K(k) are V(k) and, if visit
-    // k + 4 exists, K(k + 4) and V(k + 4); after V(k) they are K(k + 4) and
-    // V(k + 4) and, if visit k + 8 exists, K(k + 8).  The wait counts follow
-    // (wave-uniform branches).
-    auto wait_k = [&](int kk) {
-        if (kk + 4 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV + B::nK + B::nV));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
+    // Visits k0 + wave, + NWV, ... through the wave's one buffer.  Per visit:
+    // wait for its K part, copy it to registers, refill the K part with the
+    // wave's next visit (if there is one), compute the scores; then the same
+    // for the V part and PV.  The loads in flight after K(k) are V(k); after
+    // V(k), K(k + NWV) if it was issued.  The two waves sharing a SIMD overlap
+    // one's arithmetic with the other's loads.
+    auto wait_k = [&]() {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nV));
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
     };
     auto wait_v = [&](int kk) {
-        if (kk + 8 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nK + B::nV + B::nK));
-        else if (kk + 4 < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nK + B::nV));
+        if (kk + NWV < k1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(B::nK));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
     };
+    bool first = true;
     while (k < k1) {
         DecK<D> rk;
         u32x4 rv[NB];
-        wait_k(k);
+        wait_k();
         if (k == k_tok) patch_k<D>(ka, t_tok, lane, ((const u32x4*)lds_tok)[lane & (D / 8 - 1)]);
         dec_read_k<D>(c, ka, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);                                 // copied out of ka
-        if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, ka_u);
-        bf16x8 pb = dec_scores<D, true>(c, k, rk, kcr, qraw, lds_rw, o, m, l);
+        if (k + NWV < k1) dec_load_k<D, STREAM>(c, k + NWV, lane, ka_u);
+        bf16x8 pb = first ? dec_scores<D, true>(c, k, rk, lds_kc, qraw, lds_rw, o, m, l)
+                          : dec_scores<D, false>(c, k, rk, lds_kc, qraw, lds_rw, o, m, l);
+        first = false;
         wait_v(k);
         if (k == k_tok) patch_v<D>(va, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
         dec_read_v<D>(va, lane, rv);
         __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_v<D, STREAM>(c, k + 8, va_u);
+        if (k + NWV < k1) dec_load_v<D, STREAM>(c, k + NWV, va_u);
         dec_pv<D>(rv, pb, o);
-        k += 4;
-        if (k >= k1) break;
-        wait_k(k);
-        if (k == k_tok) patch_k<D>(kb, t_tok, lane, ((const u32x4*)lds_tok)[lane & (D / 8 - 1)]);
-        dec_read_k<D>(c, kb, rk);
-        __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_k<D, STREAM>(c, k + 8, lane, kb_u);
-        pb = dec_scores<D, false>(c, k, rk, kcr, qraw, lds_rw, o, m, l);
-        wait_v(k);
-        if (k == k_tok) patch_v<D>(vb, t_tok, lane, ((const u32x4*)lds_tok)[D / 8 + (lane & (D / 8 - 1))]);
-        dec_read_v<D>(vb, lane, rv);
-        __builtin_amdgcn_s_waitcnt(kLgkm0);
-        if (k + 8 < k1) dec_load_v<D, STREAM>(c, k + 8, vb_u);
-        dec_pv<D>(rv, pb, o);
-        k += 4;
+        k += NWV;
     }
     __builtin_amdgcn_s_waitcnt(0);   // every load has landed before the LDS is reused
     lds_fence();
@@ -1184,7 +1188,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         g.state[(int64_t)layer * g.n_streams + b] = ns;
     }
 
-    // Across the block's 4 waves: each wave rescales its {l, O} to the block's
+    // Across the block's waves: each wave rescales its {l, O} to the block's
     // running max before writing them, so that the per-element merge is a sum.
     // The first barrier also means every wave is done with its visit buffers,
     // which red_o overlays.
@@ -1195,7 +1199,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
         const int hn = n < G ? n : 0;
         float mb = red_ml[0][hn][0];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) mb = fmaxf(mb, red_ml[w][hn][0]);
+        for (int w = 1; w < NWV; ++w) mb = fmaxf(mb, red_ml[w][hn][0]);
         const float f = fast_exp2(m - mb);
         if (n < G) {
             if (gq == 0) red_ml[wave][n][1] = l * f;
@@ -1221,19 +1225,20 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     // children's, so results are the same run to run.  One round trip per
     // level; two splits (the usual case) take one level and no block-wide
     // count.
-    constexpr int kPer = (kMaxGroupMfma * D + 255) / 256;
+    constexpr int kThr = 64 * NWV;
+    constexpr int kPer = (kMaxGroupMfma * D + kThr - 1) / kThr;
     float p_num[kPer], p_den[kPer], p_m[kPer];
     // elements of this thread: the same count across a wave (G * D is a
     // multiple of 64), so the loops below branch uniformly
-    const int n_mine = __builtin_amdgcn_readfirstlane((G * D - 64 * wave + 255) / 256);
+    const int n_mine = __builtin_amdgcn_readfirstlane((G * D - 64 * wave + kThr - 1) / kThr);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         if (i >= n_mine) break;
-        const int idx = tid + 256 * i;
+        const int idx = tid + kThr * i;
         const int h = idx / D, d = idx - h * D;
         float mm = red_ml[0][h][0], num = red_o[0][h][d], den = red_ml[0][h][1];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) {
+        for (int w = 1; w < NWV; ++w) {
             mm = fmaxf(mm, red_ml[w][h][0]);
             num += red_o[w][h][d];
             den += red_ml[w][h][1];
@@ -1247,7 +1252,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             if (i >= n_mine) break;
-            out_at(tid + 256 * i) = f32_to_bf16_bits(p_num[i] / p_den[i]);
+            out_at(tid + kThr * i) = f32_to_bf16_bits(p_num[i] / p_den[i]);
         }
         return;
     }
@@ -1266,7 +1271,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             const bool live = p_den[i] > 0.f;
             const float on = live ? p_num[i] * __builtin_amdgcn_rcpf(p_den[i]) : 0.f;
             x_mine[i] = pack_partial(on, live ? p_m[i] + __builtin_amdgcn_logf(p_den[i]) : -INFINITY);
-            x_old[i] = __hip_atomic_exchange(slots + 256 * i, x_mine[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            x_old[i] = __hip_atomic_exchange(slots + kThr * i, x_mine[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -1278,8 +1283,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             const float wa = fast_exp2(la - mx), wb = fast_exp2(lb - mx);
             const float r = (__uint_as_float((uint32_t)a) * wa + __uint_as_float((uint32_t)c1) * wb) *
                             __builtin_amdgcn_rcpf(wa + wb);
-            out_at(tid + 256 * i) = f32_to_bf16_bits(r);
-            __hip_atomic_store(slots + 256 * i, kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            out_at(tid + kThr * i) = f32_to_bf16_bits(r);
+            __hip_atomic_store(slots + kThr * i, kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         return;
     }
@@ -1288,8 +1293,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     uint64_t xv[kPer];
     bool carry[kPer];
 #pragma unroll
+    for (int i = 0; i < kPer; ++i) carry[i] = i < n_mine;   // every entry set: the loops below test all kPer
+#pragma unroll
     for (int i = 0; i < kPer; ++i) {
-        carry[i] = i < n_mine;
         if (i >= n_mine) break;
         const bool live = p_den[i] > 0.f;             // then den >= 1 (the max term is 1)
         const float on = live ? p_num[i] * __builtin_amdgcn_rcpf(p_den[i]) : 0.f;
@@ -1303,7 +1309,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
             // every exchange of the level issued before any result is needed
 #pragma unroll
             for (int i = 0; i < kPer; ++i)
-                if (carry[i]) old[i] = __hip_atomic_exchange(sl + 256 * i, xv[i], __ATOMIC_RELAXED,
+                if (carry[i]) old[i] = __hip_atomic_exchange(sl + kThr * i, xv[i], __ATOMIC_RELAXED,
                                                              __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
@@ -1313,7 +1319,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
                     continue;
                 }
                 xv[i] = (node & 1) ? merge_partials(old[i], xv[i]) : merge_partials(xv[i], old[i]);
-                __hip_atomic_store(sl + 256 * i, kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sl + kThr * i, kSlotEmpty, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         base += width >> 1;
@@ -1322,7 +1328,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma(Geometry g, int layer, Str
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-        if (carry[i]) out_at(tid + 256 * i) = f32_to_bf16_bits(__uint_as_float((uint32_t)xv[i]));
+        if (carry[i]) out_at(tid + kThr * i) = f32_to_bf16_bits(__uint_as_float((uint32_t)xv[i]));
 }
 
 // ---------------------------------------------------------- pipelined chunk --
@@ -1936,11 +1942,11 @@ hipError_t run_portable(const Geometry& g, int layer, const StreamBatch& st, int
 template <int D>
 hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, const void* q, void* out,
                            int n_cu, const void* k_new, const void* v_new, hipStream_t s) {
-    // one resident block per CU for D = 128 (one wave per SIMD), two for D = 64;
+    // one resident block per CU (two waves per SIMD);
     // at most 8 splits, rounded down to a power of two: each level of the merge
     // tree adds an exchange latency that costs more than the shorter walks save
     // (5 splits take the 3 levels of 8, 4 take 2)
-    int n_split = min(pick_splits(st.nb * g.hkv, g.w_pad / kTile, D == 128 ? n_cu : 2 * n_cu, 4), 8);
+    int n_split = min(pick_splits(st.nb * g.hkv, g.w_pad / kTile, n_cu, 4), 8);
     n_split = n_split >= 8 ? 8 : n_split >= 4 ? 4 : n_split >= 2 ? 2 : 1;
     // three instances: the method, the method with a pinned prefix in the batch,
     // and the rebase-on-evict variant (which has no prefix)
@@ -1949,7 +1955,7 @@ hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, 
     auto kern = g.prerot ? (stream ? decode_mfma<D, true, false, true> : decode_mfma<D, true, false, false>)
               : any_prefix(st) ? (stream ? decode_mfma<D, false, true, true> : decode_mfma<D, false, true, false>)
                                : (stream ? decode_mfma<D, false, false, true> : decode_mfma<D, false, false, false>);
-    hipLaunchKernelGGL(kern, dim3(n_split, g.hkv, st.nb), dim3(256), 0, s, g, layer, st, (const uint16_t*)q,
+    hipLaunchKernelGGL(kern, dim3(n_split, g.hkv, st.nb), dim3(64 * kDecWaves), 0, s, g, layer, st, (const uint16_t*)q,
                        (uint16_t*)out, n_split, (const uint16_t*)k_new, (const uint16_t*)v_new);
     return hipGetLastError();
 }
