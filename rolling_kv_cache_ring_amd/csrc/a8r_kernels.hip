@@ -563,7 +563,8 @@ struct DecodeCtx {
     const uint16_t* vp;
     const float2* table;
     rsrc_t kr, vr, tr;     // the pair's K and V blocks and the table, as buffers
-    uint32_t koff[8];      // this lane's byte offsets inside a tile's K rows, per load
+    uint32_t koff[2];      // this lane's byte offsets inside a tile's K rows (loads j with
+                           // ((64 j / (D/8)) >> 3) even, odd; a load's rows add 1024 j)
     uint32_t voff, toff;   // ... inside a tile's V blocks, and inside a table row
     int oldest, t_o, p0t, n_tiles, L, W, rq, tb0, tb1, gq, n;
     int n_roll, F;     // visits over the ring, then ceil(F / 32) over the prefix
@@ -761,15 +762,26 @@ __device__ __forceinline__ void dma_table_row(const float2* table, int row, int 
 // dec_load_v): K row r = RPI j + lane / (D/8) of a tile, its swizzled
 // 16-byte column, for load j; the 8 slots of V dim n of the tile's 8-slot
 // block gq; 16 bytes of a table row (lanes past the row re-read its end).
+// Load j covers rows RPI j .. RPI j + RPI - 1 (RPI = 4 or 8 rows of 1024 / RPI
+// bytes): its rows start 1024 j bytes into the tile, and a row's swizzle
+// k_swz(r) takes bits 0-1 from the lane's row rl and bit 2 from (RPI j) >> 3,
+// so two per-lane offsets serve every load (fewer registers held across the
+// walk).
+template <int D>
+__device__ __forceinline__ int dec_k_class(int j) {
+    return ((64 / (D / 8)) * j >> 3) & 1;
+}
+
 template <int D>
 __device__ __forceinline__ void dec_lane_offsets(DecodeCtx& c, int lane) {
     constexpr int RPI = 64 / (D / 8);            // rows per instruction
+    static_assert(RPI == 4 || RPI == 8, "rows per load");
     const int rl = lane / (D / 8), sl = lane % (D / 8);
 #pragma unroll
-    for (int j = 0; j < 2 * (D / 32); ++j) {
-        const int r = RPI * j + rl;
+    for (int cls = 0; cls < 2; ++cls) {
+        const int r = rl + 8 * cls;              // a row with the class's swizzle
         const int col = 8 * (sl >> 3) + ((sl & 7) ^ k_swz(r));
-        c.koff[j] = (uint32_t)((r * D + 8 * col) * 2);
+        c.koff[cls] = (uint32_t)((rl * D + 8 * col) * 2);
     }
     c.voff = (uint32_t)(((c.gq * D + c.n) * 8) * 2);
     c.toff = (uint32_t)(16 * lane < 4 * D ? 16 * lane : 4 * D - 16);
@@ -780,7 +792,8 @@ __device__ __forceinline__ void dec_load_k(const DecodeCtx& c, int k, int lane, 
     const VisitSrc vs = visit_src(c, k);
     const uint32_t tile_off = (uint32_t)vs.tile * (kTile * D * 2);
 #pragma unroll
-    for (int j = 0; j < 2 * (D / 32); ++j) bdma16<STREAM>(c.kr, c.koff[j], tile_off, kbuf + j * 1024);
+    for (int j = 0; j < 2 * (D / 32); ++j)
+        bdma16<STREAM>(c.kr, c.koff[dec_k_class<D>(j)], tile_off + 1024 * j, kbuf + j * 1024);
     bdma16<false>(c.tr, c.toff, (uint32_t)(c.rq - (c.prerot ? 0 : vs.rho)) * (D * 4), kbuf + 2 * (D / 32) * 1024);
 }
 
@@ -1124,13 +1137,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_mfma(Geometry g, int
     __builtin_amdgcn_s_barrier();                                    // ... and every other wave's
     lds_fence();
 
-    // the query stays as bf16 bits (the softmax scale is applied to the scores)
+    // the query stays as bf16 bits (the softmax scale is applied to the
+    // scores), held in registers; the prefix instance, short of registers,
+    // re-reads it from LDS at every visit instead (held there it spilled, and
+    // the spill reloads' waits drained the walk's loads)
+    const unsigned char* qrow = lds_q + (n < G ? n : 0) * D * 2 + 16 * gq;
     u32x4 qraw[KK];
-    {
-        const unsigned char* qrow = lds_q + (n < G ? n : 0) * D * 2 + 16 * gq;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qraw[kk] = *(const u32x4*)(qrow + 64 * kk);
-    }
+    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *(const u32x4*)(qrow + 64 * kk);
 
     floatx4 o[NB];
 #pragma unroll
@@ -1163,6 +1177,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_mfma(Geometry g, int
         dec_read_k<D>(c, ka, rk);
         __builtin_amdgcn_s_waitcnt(kLgkm0);                                 // copied out of ka
         if (k + NWV < k1) dec_load_k<D, STREAM>(c, k + NWV, lane, ka_u);
+        if (PRE) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) qraw[kk] = *(const u32x4*)(qrow + 64 * kk);
+        }
         bf16x8 pb = first ? dec_scores<D, true>(c, k, rk, lds_kc, qraw, lds_rw, o, m, l)
                           : dec_scores<D, false>(c, k, rk, lds_kc, qraw, lds_rw, o, m, l);
         first = false;
@@ -1942,12 +1960,13 @@ hipError_t run_portable(const Geometry& g, int layer, const StreamBatch& st, int
 template <int D>
 hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, const void* q, void* out,
                            int n_cu, const void* k_new, const void* v_new, hipStream_t s) {
-    // one resident block per CU (two waves per SIMD);
-    // at most 8 splits, rounded down to a power of two: each level of the merge
-    // tree adds an exchange latency that costs more than the shorter walks save
-    // (5 splits take the 3 levels of 8, 4 take 2)
-    int n_split = min(pick_splits(st.nb * g.hkv, g.w_pad / kTile, n_cu, 4), 8);
-    n_split = n_split >= 8 ? 8 : n_split >= 4 ? 4 : n_split >= 2 ? 2 : 1;
+    // one resident block per CU (two waves per SIMD); the split count is
+    // rounded down to a power of two: each level of the merge tree adds an
+    // exchange latency (about 1.4 us), so a count between two powers pays the
+    // upper one's levels for less walk saved (one 3B stream: 16 splits, one
+    // visit per wave, 11.0 us; 8 splits 11.9; 4 splits 15.2)
+    int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, n_cu, 4);
+    n_split = n_split >= 16 ? 16 : n_split >= 8 ? 8 : n_split >= 4 ? 4 : n_split >= 2 ? 2 : 1;
     // three instances: the method, the method with a pinned prefix in the batch,
     // and the rebase-on-evict variant (which has no prefix)
     // streaming loads when the launch's windows exceed the chip's L2 (8 x 4 MB)

@@ -303,3 +303,45 @@ def test_policies_agree():
     assert np.max(np.abs(oa - ob)) < 2e-2
     a.close()
     b.close()
+
+
+@pytest.mark.parametrize("window,hq,hkv,d", [
+    (2048, 16, 2, 128), (4096, 32, 2, 128), (1024, 8, 1, 64), (4096, 8, 4, 128),
+])
+def test_decode_writes_only_its_rows(window, hq, hkv, d):
+    """Decode and fused append + decode with eight key splits (three levels of
+    the merge tree) write their output rows and nothing past them: the output
+    is a view at the start of a larger buffer whose tail holds a sentinel, and
+    the rows match the oracle.  Groups of 8 and 16 query heads per KV head
+    give each thread of the merge a partial and a full share of elements."""
+    say("decode_writes_only_its_rows", window, hq, hkv, d)
+    from gpu_util import torch, to_host_f64
+    t = torch()
+    rng = np.random.default_rng(window + 7 * hq + d)
+    nb = 2
+    tw = Twin(1, nb, hq, hkv, d, window, 256, True, False)
+    tw.reset(0, [3 * window + 11, 2**24 + 5], [int(rng.integers(window)), int(rng.integers(window))])
+    for n in [256] * (window // 256 - 1) + [255]:          # window - 1 tokens
+        tw.append(0, 0, rand(rng, nb, n, hkv, d), rand(rng, nb, n, hkv, d))
+    sentinel = 0x7f7f                                       # bf16 bits of a huge finite value
+    for step in range(3):
+        q = rand(rng, nb, hq, d)
+        big = t.full((nb + 3, hq, d), sentinel, dtype=t.int16, device="cuda")
+        if step == 1:
+            k, v = rand(rng, nb, 1, hkv, d), rand(rng, nb, 1, hkv, d)
+            tw.gpu.append_decode_attn(0, 0, nb, to_device(k, True), to_device(v, True), to_device(q, True),
+                                      big[:nb])
+            tw.ora.append(0, 0, k, v)
+        else:
+            tw.gpu.decode_attn(0, 0, nb, to_device(q, True), big[:nb])
+        tail = big[nb:].cpu().numpy()
+        assert np.all(tail == sentinel), ("output written past its rows", step, int(np.sum(tail != sentinel)))
+        tw._cmp(to_host_f64(big[:nb], True), tw.ora.decode(0, 0, q), ("decode", step))
+    # one stream of the two: the other stream's rows stay untouched too
+    q = rand(rng, 1, hq, d)
+    big = t.full((4, hq, d), sentinel, dtype=t.int16, device="cuda")
+    tw.gpu.decode_attn(0, 1, 1, to_device(q, True), big[:1])
+    assert np.all(big[1:].cpu().numpy() == sentinel)
+    tw._cmp(to_host_f64(big[:1], True), tw.ora.decode(0, 1, q), ("decode", "stream 1"))
+    say("worst err", tw.worst)
+    tw.close()
