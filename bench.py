@@ -85,11 +85,22 @@ def copy_probe(torch):
 
 # kernels of one attention call (what roofline.achieved times): the fused or
 # separate attention kernel and, for split chunks, the split merge
-CALL_KERNELS = ("decode_mfma", "chunk_pipe", "combine_kernel", "attn_portable")
+CALL_KERNELS = ("decode_mfma", "chunk_pipe", "combine_kernel", "attn_portable", "rebase_kernel")
 
 
 def short_name(name):
     return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def profile_key(args):
+    """The key of a run's counters in profiles/pmc_traffic.json: the workload,
+    the pinned prefix and the cache mode (each changes what a call moves)."""
+    key = args.workload
+    if getattr(args, "prefix", 0):
+        key += f"+prefix{args.prefix}"
+    if getattr(args, "cache_mode", "rotate_on_read") == "rebase_on_evict":
+        key += "+rebase_on_evict"
+    return key
 
 
 def kernel_family(name):
@@ -190,7 +201,7 @@ def summarize(args):
             rec = json.load(open(rec_path))
         except (OSError, ValueError):
             rec = {}
-        key = args.workload + (f"+prefix{args.prefix}" if args.prefix else "")
+        key = profile_key(args)
         entry = rec.get(key, {})
         if entry.get("kernel_sha256_16") != kernel_hash():
             entry = {}      # counters taken on an older kernel source no longer apply
@@ -514,7 +525,7 @@ def main():
     bytes_step = NL * (float(np.mean([algorithmic_bytes(wl, lv) for lv in lives])) + append_bytes(wl))
     gbps_step = bytes_step * steps_per_s / 1e9
     achieved = bytes_launch / (attn_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(args.workload + (f"+prefix{F}" if F else ""))
+    traffic = traffic_from_profiles(profile_key(args))
 
     rebuild = rebuild_timing(args, torch, cache, wl, ms, gen) if args.rebuild else None
 
