@@ -1233,8 +1233,8 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_mfma(Geometry g, int
     //
     // The splits of one (stream, KV head) merge per output element in a fixed
     // binary tree: at each level the nodes 2m and 2m + 1 (splits at the first
-    // level; an odd last node passes up unchanged) meet in an exchange slot that
-    // holds kSlotEmpty between calls.  Each carrier swaps in its node's
+    // level; the launcher passes a power of two, so every node has its partner)
+    // meet in an exchange slot that holds kSlotEmpty between calls.  Each carrier swaps in its node's
     // normalized partial (O / l, m + log2 l) with one 64-bit atomic exchange;
     // the one that gets its partner's partial back (it came second) merges the
     // two (node 2m always as the first operand), empties the slot and carries
@@ -1321,7 +1321,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_mfma(Geometry g, int
     }
     int node = split, width = n_split, base = 0;   // wave-uniform
     while (width > 1) {
-        if ((node ^ 1) < width) {
+        {
             uint64_t* sl = slots + (base + (node >> 1)) * node_stride;
             uint64_t old[kPer];
             // every exchange of the level issued before any result is needed
@@ -1342,7 +1342,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void decode_mfma(Geometry g, int
         }
         base += width >> 1;
         node >>= 1;
-        width = (width + 1) >> 1;
+        width >>= 1;
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
@@ -1966,7 +1966,8 @@ hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, 
     // upper one's levels for less walk saved (one 3B stream: 16 splits, one
     // visit per wave, 11.0 us; 8 splits 11.9; 4 splits 15.2)
     int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, n_cu, 4);
-    n_split = n_split >= 16 ? 16 : n_split >= 8 ? 8 : n_split >= 4 ? 4 : n_split >= 2 ? 2 : 1;
+    n_split = n_split >= 16 ? 16 : n_split >= 8 ? 8 : n_split >= 4 ? 4 : n_split >= 2 ? 2 : 1;   // the merge tree
+                                                                                               // needs a power of two
     // three instances: the method, the method with a pinned prefix in the batch,
     // and the rebase-on-evict variant (which has no prefix)
     // streaming loads when the launch's windows exceed the chip's L2 (8 x 4 MB)
