@@ -45,17 +45,17 @@ def command(out: str = LIB) -> list[str]:
             *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
 
 
-def resource_usage(out_dir: str) -> dict[str, dict[str, int]]:
-    """Compiles the kernels' device code once more (an object file under
-    out_dir) with the backend's resource remarks and returns, per kernel
-    symbol, its VGPRs, AGPRs, scratch bytes per lane, occupancy (waves per
-    SIMD) and LDS bytes per block."""
+def compile_device(out_dir: str) -> tuple[dict[str, dict[str, int]], str]:
+    """Compiles the kernels' device code once more, to assembly under out_dir,
+    with the backend's resource remarks.  Returns, per kernel symbol, its VGPRs,
+    AGPRs, scratch bytes per lane, occupancy (waves per SIMD) and LDS bytes per
+    block, and the assembly text."""
     import re
-    obj = os.path.join(out_dir, "a8r_kernels_device.o")
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c", "--cuda-device-only",
+    asm = os.path.join(out_dir, "a8r_kernels_device.s")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-S", "--cuda-device-only",
            "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-Rpass-analysis=kernel-resource-usage",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, "a8r_kernels.hip"), "-o", obj]
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, "a8r_kernels.hip"), "-o", asm]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr[-4000:]}")
@@ -71,7 +71,8 @@ def resource_usage(out_dir: str) -> dict[str, dict[str, int]]:
         m = re.search(r"remark:\s+(.+?): (\d+)", line)
         if cur is not None and m and m.group(1) in keys:
             cur[keys[m.group(1)]] = int(m.group(2))
-    return usage
+    with open(asm) as f:
+        return usage, f.read()
 
 
 def build(verbose: bool = False) -> str:
