@@ -53,6 +53,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegBig = -1.0e30f;   // running-max seed: exp2(x - kNegBig) never NaNs
@@ -319,10 +320,11 @@ __global__ __launch_bounds__(256) void combine_kernel(Geometry g, int n_q, int n
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const int64_t pr = part_row(g, bi, kh, s < n_split ? s : n_split - 1, row);
-        const float2 ml = *(const float2*)&g.part_ml[pr * 2];
+        const floatx2 ml = __builtin_nontemporal_load((const floatx2*)&g.part_ml[pr * 2]);   // read once
         mv[s] = ml.x;
         lv[s] = ml.y;
-        ov[s] = *(const float4*)&g.part_o[pr * D + 4 * d4];
+        const floatx4 ox = __builtin_nontemporal_load((const floatx4*)&g.part_o[pr * D + 4 * d4]);
+        ov[s] = float4{ox[0], ox[1], ox[2], ox[3]};
     }
     __builtin_amdgcn_sched_barrier(0);                 // every load issued before the merge
     float mmax = mv[0], den = lv[0];
@@ -1905,13 +1907,15 @@ __global__ __launch_bounds__(256 * WG, 1) void chunk_pipe(Geometry g, int layer,
 #pragma unroll
                 for (int j = 0; j < 4; ++j) op[16 * nb + 4 * gq + j] = f32_to_bf16_bits(o[w][nb][j] * inv);
         } else {
-            // partials for combine_kernel (launched next on the same stream)
+            // partials for combine_kernel (launched next on the same stream),
+            // stored non-temporal: read once, mostly by blocks on other XCDs
+            // (0.3-0.5 us per call less than through the L2)
             const int64_t pr = part_row(g, bi, kh, split, row);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                *(float4*)&g.part_o[pr * D + 16 * nb + 4 * gq] =
-                    float4{o[w][nb][0], o[w][nb][1], o[w][nb][2], o[w][nb][3]};
-            if (gq == 0) *(float2*)&g.part_ml[pr * 2] = float2{m[w], l[w]};
+                __builtin_nontemporal_store(floatx4{o[w][nb][0], o[w][nb][1], o[w][nb][2], o[w][nb][3]},
+                                            (floatx4*)&g.part_o[pr * D + 16 * nb + 4 * gq]);
+            if (gq == 0) __builtin_nontemporal_store(floatx2{m[w], l[w]}, (floatx2*)&g.part_ml[pr * 2]);
         }
     }
 }
