@@ -290,8 +290,9 @@ a8r_status a8r_append_chunk_attn(a8r_cache* cache, int32_t layer, int32_t b0, in
  * prefix is kept.  16-byte aligned pointers, 1 <= n <= W, n <= P,
  * hidden_dim a multiple of 64 (at most 65536).  Asynchronous on the cache's
  * stream.  Errors: EINVAL, EUNSUPPORTED (float32 caches, A8R_REBASE_ON_EVICT,
- * n_kv_heads * head_dim not a multiple of 128), EDEVICE; nothing changes on
- * error. */
+ * n_kv_heads * head_dim not a multiple of 128, n * hidden_dim * 2 >= 2^31
+ * bytes per stream), EDEVICE; nothing changes on error.  Slots of the last
+ * 8-slot block past n (not live) are overwritten with token n - 1's V. */
 a8r_status a8r_rebuild_window(a8r_cache* cache, int32_t layer, int32_t b0, int32_t nb, int32_t n,
                               int32_t hidden_dim, const void* hidden, const void* w_k, const void* w_v);
 

@@ -578,6 +578,9 @@ a8r_status a8r_rebuild_window(a8r_cache* c, int32_t layer, int32_t b0, int32_t n
     if (n < 1 || n > c->cfg.window) return fail(A8R_EINVAL, "n %d out of [1, W=%d]", n, c->cfg.window);
     if (hidden_dim < 64 || hidden_dim % 64 || hidden_dim > (1 << 16))
         return fail(A8R_EINVAL, "hidden_dim %d must be a positive multiple of 64, at most 65536", hidden_dim);
+    if ((int64_t)n * hidden_dim * 2 >= ((int64_t)1 << 31))   // the kernel's 32-bit offsets into one stream's rows
+        return fail(A8R_EUNSUPPORTED, "window rebuild needs n * hidden_dim * 2 < 2^31 bytes per stream (got %lld)",
+                    (long long)n * hidden_dim * 2);
     if (!hidden || !w_k || !w_v) return fail(A8R_EINVAL, "hidden, w_k or w_v is NULL");
     if (!aligned16(hidden) || !aligned16(w_k) || !aligned16(w_v))
         return fail(A8R_EINVAL, "hidden, w_k and w_v must be 16-byte aligned");

@@ -2010,28 +2010,35 @@ hipError_t run_chunk_pipe(const Geometry& g, int layer, const StreamBatch& st, i
 // to bf16 (nearest even).  Token j of the window goes to ring slot j: K rows as
 // appended, V into its transposed 8-slot block.
 //
-// One block of 4 waves per (128-token tile of one stream, 128 output columns);
-// the columns are K's Hkv*D then V's.  Waves take 64 x 64 quarters of the tile
-// (4 x 4 MFMA tiles each).  A and B (both k-contiguous) are staged through LDS
-// in 64-wide k steps, double-buffered, rows padded by 16 bytes so that the
-// operand reads of eight consecutive lanes (eight rows) fall on distinct banks.
-// The blocks of one token tile are 8 block ids apart, so they run on one XCD
-// and read the token tile from HBM once.  The epilogue stages the bf16 tile in
-// LDS and writes whole 16-byte chunks: K rows, or 8 consecutive slots of one
-// dim for V.  Tokens past n load as zeros; their V entries in the last 8-slot
-// block are written as zeros (those slots are not live).
-constexpr int kRbM = 128, kRbN = 128, kRbK = 64;
-constexpr int kRbRow = kRbK * 2 + 16;                  // LDS bytes per staged row (A or B)
+// One block of 8 waves per (256-token tile of one stream, 128 output columns);
+// the columns are K's Hkv*D then V's.  Waves take 64 x 64 pieces of the tile
+// (4 x 4 MFMA tiles each).  A (the hidden states) and B (the weight rows, both
+// k-contiguous) come into LDS with direct global->LDS buffer loads, 64-wide k
+// steps, three stages deep with exact vmcnt waits (the k step's latency was
+// what the single-stage register staging of an earlier form waited on).  A
+// staged row of 64 k is 8 chunks of 16 bytes, chunk c at position c ^ (row %
+// 8), so the operand reads of eight consecutive lanes (rows) fall on distinct
+// banks.  Rows of the tile past token n re-read token n - 1, so every load
+// stays inside the stream's hidden states.  The blocks of one token tile are
+// 8 block ids apart, so they run on one XCD and read the token tile from HBM
+// once.  The epilogue stages the bf16 tile in LDS and writes whole 16-byte
+// chunks: K rows, or 8 consecutive slots of one dim for V.  Tokens past n are
+// not written, except in V's last 8-slot block, whose slots past n (not live,
+// masked out of every attention) get token n - 1's values.
+constexpr int kRbM = 256, kRbN = 128, kRbK = 64, kRbStages = 3;
+constexpr int kRbStageA = kRbM * kRbK * 2, kRbStageB = kRbN * kRbK * 2;
+constexpr int kRbStage = kRbStageA + kRbStageB;
 constexpr int kRbOut = kRbN * 2 + 16;                  // LDS bytes per epilogue row
 
-__global__ __launch_bounds__(256, 2) void rebuild_kernel(Geometry g, int layer, StreamBatch st, int n, int hidden,
+__global__ __launch_bounds__(512, 1) void rebuild_kernel(Geometry g, int layer, StreamBatch st, int n, int hidden,
                                                          const uint16_t* __restrict__ h,
                                                          const uint16_t* __restrict__ wk,
                                                          const uint16_t* __restrict__ wv, int n_row_tiles,
                                                          int n_col_tiles) {
-    __shared__ __align__(16) unsigned char lds[2 * 2 * kRbM * kRbRow];   // [buffer][A, B][128 rows]
-    static_assert(kRbM * kRbOut <= 2 * 2 * kRbM * kRbRow, "epilogue tile does not fit");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ __align__(16) unsigned char lds[kRbStages * kRbStage];
+    static_assert(kRbM * kRbOut <= kRbStages * kRbStage, "epilogue tile does not fit");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, gq = lane >> 4;
     // block id -> (stream, token tile, column tile): the column tiles of one
     // token tile are 8 ids apart (one XCD)
@@ -2043,29 +2050,30 @@ __global__ __launch_bounds__(256, 2) void rebuild_kernel(Geometry g, int layer, 
     const int D = g.d, kvd = g.hkv * D, col0 = col_t * kRbN;
     const bool is_v = col0 >= kvd;
     const uint16_t* w = is_v ? wv + (int64_t)(col0 - kvd) * hidden : wk + (int64_t)col0 * hidden;
-    const uint16_t* hrow = h + (int64_t)bi * n * hidden;
+    // the stream's hidden states, tokens 0 .. n - 1 (n * hidden * 2 < 2^31,
+    // checked by the host)
+    const rsrc_t ra = make_rsrc(h + (int64_t)bi * n * hidden, (uint32_t)n * hidden * 2);
+    const rsrc_t rw = make_rsrc(w, (uint32_t)kRbN * hidden * 2);
 
-    // staging: each thread moves 4 chunks of 16 bytes of A and of B per k step
-    // (128 rows x 128 bytes each): row tid / 8 + 32 u, chunk tid % 8
-    const int sr = tid >> 3, sc = tid & 7;
-    u32x4 ra[4], rb[4];
-    auto load = [&](int k0) {
+    // DMA of one stage: instruction j moves rows 8j .. 8j+7 (1 KiB); lane l
+    // writes LDS chunk l % 8 of row 8j + l / 8 with source chunk
+    // (l % 8) ^ (l / 8).  A: 32 instructions, 4 per wave; B: 16, 2 per wave.
+    constexpr int nA = kRbM / 8 / 8, nB = kRbN / 8 / 8, nL = nA + nB;   // per wave
+    const uint32_t lane_src = (uint32_t)(16 * ((lane & 7) ^ (lane >> 3)));
+    uint32_t va[nA], vb[nB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = sr + 32 * u;
-            const int tok = row0 + r;
-            ra[u] = tok < n ? *(const u32x4*)(hrow + (int64_t)tok * hidden + k0 + 8 * sc) : u32x4{0u, 0u, 0u, 0u};
-            rb[u] = *(const u32x4*)(w + (int64_t)r * hidden + k0 + 8 * sc);
-        }
-    };
-    auto stage = [&](int buf) {
-        unsigned char* a = lds + buf * 2 * kRbM * kRbRow;
-        unsigned char* b = a + kRbM * kRbRow;
+    for (int u = 0; u < nA; ++u)
+        va[u] = (uint32_t)min(row0 + 8 * (wave * nA + u) + (lane >> 3), n - 1) * hidden * 2 + lane_src;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            *(u32x4*)(a + (sr + 32 * u) * kRbRow + 16 * sc) = ra[u];
-            *(u32x4*)(b + (sr + 32 * u) * kRbRow + 16 * sc) = rb[u];
-        }
+    for (int u = 0; u < nB; ++u) vb[u] = (uint32_t)(8 * (wave * nB + u) + (lane >> 3)) * hidden * 2 + lane_src;
+    const uint32_t lds_u = lds_u32(lds);
+    auto issue = [&](int kt) {
+        const uint32_t st_u = lds_u + (uint32_t)((kt % kRbStages) * kRbStage);
+        const uint32_t koff = (uint32_t)kt * kRbK * 2;
+#pragma unroll
+        for (int u = 0; u < nA; ++u) bdma16<false>(ra, va[u], koff, st_u + 1024 * (wave * nA + u));
+#pragma unroll
+        for (int u = 0; u < nB; ++u) bdma16<false>(rw, vb[u], koff, st_u + kRbStageA + 1024 * (wave * nB + u));
     };
 
     // wave (wm, wn) computes rows 64 wm .., columns 64 wn ..
@@ -2075,23 +2083,30 @@ __global__ __launch_bounds__(256, 2) void rebuild_kernel(Geometry g, int layer, 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // a lane's operand rows 64 wm + 16 i + n16 (A) and 64 wn + 16 j + n16 (B):
+    // row % 8 = n16 % 8 for every i, j
+    const int swz = n16 & 7;
 
     const int n_k = hidden / kRbK;
-    load(0);
-    stage(0);
-    __syncthreads();
+    issue(0);
+    if (n_k > 1) issue(1);
     for (int kt = 0; kt < n_k; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < n_k) load((kt + 1) * kRbK);          // next step's operands in flight
-        const unsigned char* a = lds + buf * 2 * kRbM * kRbRow;
-        const unsigned char* b = a + kRbM * kRbRow;
+        // stage kt has landed once at most stage kt + 1's loads are outstanding
+        if (kt + 1 < n_k) __builtin_amdgcn_s_waitcnt(vmcnt_imm(nL));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();                  // every wave's share; stage kt - 1 is free
+        __builtin_amdgcn_sched_barrier(0);
+        lds_fence();
+        if (kt + 2 < n_k) issue(kt + 2);
+        const int so = (kt % kRbStages) * kRbStage;
 #pragma unroll
         for (int kb = 0; kb < kRbK / 32; ++kb) {
+            const int ch = 16 * ((4 * kb + gq) ^ swz);
             bf16x8 af[4], bf[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                af[i] = *(const bf16x8*)(a + (64 * wm + 16 * i + n16) * kRbRow + 2 * (32 * kb + 8 * gq));
-                bf[i] = *(const bf16x8*)(b + (64 * wn + 16 * i + n16) * kRbRow + 2 * (32 * kb + 8 * gq));
+                af[i] = *(const bf16x8*)(lds + so + (64 * wm + 16 * i + n16) * (kRbK * 2) + ch);
+                bf[i] = *(const bf16x8*)(lds + so + kRbStageA + (64 * wn + 16 * i + n16) * (kRbK * 2) + ch);
             }
             // C^T tile (i, j): rows = output columns (B), columns = tokens (A),
             // so a lane holds 4 consecutive columns of one token
@@ -2101,11 +2116,9 @@ __global__ __launch_bounds__(256, 2) void rebuild_kernel(Geometry g, int layer, 
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < n_k) {
-            stage(buf ^ 1);        // the other buffer: last read in step kt - 1, before its barrier
-            __syncthreads();
-        }
+        __builtin_amdgcn_s_waitcnt(kLgkm0);            // this wave's reads of stage kt are done
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();               // every wave is done with the operand buffers
 
     // epilogue: bf16 tile [token][column] in LDS, then 16-byte global stores
@@ -2124,8 +2137,8 @@ __global__ __launch_bounds__(256, 2) void rebuild_kernel(Geometry g, int layer, 
     __syncthreads();
     const int b = st.b0 + bi;
     if (!is_v) {
-        // 128 tokens x 16 chunks of 16 bytes (128 columns: one or two heads)
-        for (int t = tid; t < kRbM * (kRbN / 8); t += 256) {
+        // 256 tokens x 16 chunks of 16 bytes (128 columns: one or two heads)
+        for (int t = tid; t < kRbM * (kRbN / 8); t += 512) {
             const int tok = t >> 4, ch = t & 15;
             if (row0 + tok >= n) continue;
             const int col = col0 + 8 * ch, kh = col / D, d = col % D;
@@ -2133,8 +2146,8 @@ __global__ __launch_bounds__(256, 2) void rebuild_kernel(Geometry g, int layer, 
             *(u32x4*)dst = *(const u32x4*)(lds + tok * kRbOut + 16 * ch);
         }
     } else {
-        // 16 groups of 8 slots x 128 dims: 8 consecutive slots of one dim
-        for (int t = tid; t < (kRbM / 8) * kRbN; t += 256) {
+        // 32 groups of 8 slots x 128 dims: 8 consecutive slots of one dim
+        for (int t = tid; t < (kRbM / 8) * kRbN; t += 512) {
             const int grp = t / kRbN, c = t % kRbN;
             if (row0 + 8 * grp >= n) continue;
             const int col = col0 - kvd + c, kh = col / D, d = col % D;
@@ -2305,7 +2318,7 @@ hipError_t launch_rebuild(const Geometry& g, int layer, const StreamBatch& st, i
     const int n_col_tiles = 2 * g.hkv * g.d / kRbN;
     const int tiles = st.nb * n_row_tiles;
     const int blocks = 8 * n_col_tiles * ((tiles + 7) / 8);
-    hipLaunchKernelGGL(rebuild_kernel, dim3(blocks), dim3(256), 0, s, g, layer, st, n, hidden, (const uint16_t*)h,
+    hipLaunchKernelGGL(rebuild_kernel, dim3(blocks), dim3(512), 0, s, g, layer, st, n, hidden, (const uint16_t*)h,
                        (const uint16_t*)wk, (const uint16_t*)wv, n_row_tiles, n_col_tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
