@@ -307,11 +307,14 @@ class Cache:
             cache_destroy(self.handle)
             self.handle = None
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # a cache still open when the interpreter shuts down is left to the
         # process exit: the HIP runtime may already be gone, and destroy
-        # synchronizes a stream and frees device memory
-        if sys.is_finalizing():
+        # synchronizes a stream and frees device memory (the check is bound
+        # when the class is made: module globals may be gone by then)
+        if not getattr(self, "handle", None):
+            return
+        if _finalizing():
             self.handle = None
             return
         self.close()

@@ -14,8 +14,9 @@ trimming).  Checked against oracle/prefill.py:
   steps continuing from it (the appended tokens bit for bit in the ring), within
   the bf16 tolerance of the oracle's window (the exact projection rounded to
   bf16);
-* full and ragged windows (n = W, n not a multiple of 8 or 128), D = 128 and
-  D = 64, several streams of one batch, a pinned prefix kept;
+* full and ragged windows (n = W, n not a multiple of 8 or 256, n = 1), hidden
+  sizes of one to eight 64-wide k steps, D = 128 and D = 64, several streams of
+  one batch, a pinned prefix kept;
 * errors that change nothing: n > W, a window before position 0, hidden sizes
   not a multiple of 64, float32 caches, the rebase-on-evict mode.
 """
@@ -50,6 +51,8 @@ def check_projection(got, exact, bound):
     (16, 2, 128, 512, 256, 300, 3, 0),
     (8, 2, 64, 256, 128, 131, 2, 0),
     (16, 2, 128, 384, 512, 200, 2, 20),
+    (16, 2, 128, 256, 64, 1, 2, 0),                   # one token, one 64-wide k step
+    (8, 2, 64, 1024, 192, 1000, 1, 0),                # four 256-token tiles, the last ragged; three k steps
 ])
 def test_rebuild_matches_projection(hq, hkv, d, w, hidden, n, nb, prefix):
     say("rebuild", hq, hkv, d, w, hidden, n, nb, prefix)
