@@ -1,6 +1,6 @@
 """Register, scratch and LDS budgets and the memory waits of the device code,
-from the compiler's resource remarks and the assembly of this build (no GPU
-needed).
+from the compiler's resource remarks and the assembly it produces for the
+kernels (no GPU needed).
 
 A kernel that spills to scratch is slow here in a way that tests of results
 never show: scratch reloads are counted with the vector-memory loads, so the
