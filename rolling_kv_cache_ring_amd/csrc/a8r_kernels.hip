@@ -2010,33 +2010,37 @@ hipError_t run_chunk_pipe(const Geometry& g, int layer, const StreamBatch& st, i
 // to bf16 (nearest even).  Token j of the window goes to ring slot j: K rows as
 // appended, V into its transposed 8-slot block.
 //
-// One block of 8 waves per (256-token tile of one stream, 128 output columns);
-// the columns are K's Hkv*D then V's.  Waves take 64 x 64 pieces of the tile
-// (4 x 4 MFMA tiles each).  A (the hidden states) and B (the weight rows, both
-// k-contiguous) come into LDS with direct global->LDS buffer loads, 64-wide k
-// steps, three stages deep with exact vmcnt waits (the k step's latency was
-// what the single-stage register staging of an earlier form waited on).  A
-// staged row of 64 k is 8 chunks of 16 bytes, chunk c at position c ^ (row %
-// 8), so the operand reads of eight consecutive lanes (rows) fall on distinct
-// banks.  Rows of the tile past token n re-read token n - 1, so every load
-// stays inside the stream's hidden states.  The blocks of one token tile are
-// 8 block ids apart, so they run on one XCD and read the token tile from HBM
-// once.  The epilogue stages the bf16 tile in LDS and writes whole 16-byte
-// chunks: K rows, or 8 consecutive slots of one dim for V.  Tokens past n are
-// not written, except in V's last 8-slot block, whose slots past n (not live,
+// One block of 16 waves per (256-token tile of one stream, 256 output
+// columns); the columns are K's Hkv*D then V's, and a tile may hold both (its
+// K columns go to the K ring, its V columns to the V ring).  Waves take 64 x 64
+// pieces of the tile (4 x 4 MFMA tiles each).  A (the hidden states) and B (the
+// weight rows, both k-contiguous) come into LDS with direct global->LDS buffer
+// loads in 64-wide k steps, double-buffered with exact vmcnt waits.  The tile
+// size is set by the L2: the walk's operands come from it, not from HBM (each
+// token tile is read from HBM once and by every column tile from L2), and a
+// 256 x 256 tile moves half the L2 bytes per product of a 256 x 128 one (0.53
+// against 0.62 ms per layer, the 256 x 128 form three stages deep).  A staged
+// row of 64 k is 8 chunks of 16 bytes, chunk c at position c ^ (row % 8), so
+// the operand reads of eight consecutive lanes (rows) fall on distinct banks.
+// Rows of the tile past token n re-read token n - 1, so every load stays
+// inside the stream's hidden states.  The blocks of one token tile are 8 block
+// ids apart, so they run on one XCD and read the token tile from HBM once.
+// The epilogue stages the bf16 tile in LDS and writes whole 16-byte chunks: K
+// rows, or 8 consecutive slots of one dim for V.  Tokens past n are not
+// written, except in V's last 8-slot block, whose slots past n (not live,
 // masked out of every attention) get token n - 1's values.
-constexpr int kRbM = 256, kRbN = 128, kRbK = 64, kRbStages = 3;
+constexpr int kRbM = 256, kRbN = 256, kRbK = 64, kRbStages = 2;
 constexpr int kRbStageA = kRbM * kRbK * 2, kRbStageB = kRbN * kRbK * 2;
 constexpr int kRbStage = kRbStageA + kRbStageB;
 constexpr int kRbOut = kRbN * 2 + 16;                  // LDS bytes per epilogue row
+constexpr int kRbLds = kRbStages * kRbStage > kRbM * kRbOut ? kRbStages * kRbStage : kRbM * kRbOut;
 
-__global__ __launch_bounds__(512, 1) void rebuild_kernel(Geometry g, int layer, StreamBatch st, int n, int hidden,
-                                                         const uint16_t* __restrict__ h,
-                                                         const uint16_t* __restrict__ wk,
-                                                         const uint16_t* __restrict__ wv, int n_row_tiles,
-                                                         int n_col_tiles) {
-    __shared__ __align__(16) unsigned char lds[kRbStages * kRbStage];
-    static_assert(kRbM * kRbOut <= kRbStages * kRbStage, "epilogue tile does not fit");
+__global__ __launch_bounds__(1024, 1) void rebuild_kernel(Geometry g, int layer, StreamBatch st, int n, int hidden,
+                                                          const uint16_t* __restrict__ h,
+                                                          const uint16_t* __restrict__ wk,
+                                                          const uint16_t* __restrict__ wv, int n_row_tiles,
+                                                          int n_col_tiles) {
+    __shared__ __align__(16) unsigned char lds[kRbLds];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, gq = lane >> 4;
@@ -2048,24 +2052,28 @@ __global__ __launch_bounds__(512, 1) void rebuild_kernel(Geometry g, int layer, 
     if (tile >= st.nb * n_row_tiles) return;
     const int bi = tile / n_row_tiles, row0 = (tile % n_row_tiles) * kRbM;
     const int D = g.d, kvd = g.hkv * D, col0 = col_t * kRbN;
-    const bool is_v = col0 >= kvd;
-    const uint16_t* w = is_v ? wv + (int64_t)(col0 - kvd) * hidden : wk + (int64_t)col0 * hidden;
     // the stream's hidden states, tokens 0 .. n - 1 (n * hidden * 2 < 2^31,
-    // checked by the host)
+    // checked by the host); the K and V weight rows
     const rsrc_t ra = make_rsrc(h + (int64_t)bi * n * hidden, (uint32_t)n * hidden * 2);
-    const rsrc_t rw = make_rsrc(w, (uint32_t)kRbN * hidden * 2);
+    const rsrc_t rk = make_rsrc(wk, (uint32_t)kvd * hidden * 2);
+    const rsrc_t rv = make_rsrc(wv, (uint32_t)kvd * hidden * 2);
 
     // DMA of one stage: instruction j moves rows 8j .. 8j+7 (1 KiB); lane l
     // writes LDS chunk l % 8 of row 8j + l / 8 with source chunk
-    // (l % 8) ^ (l / 8).  A: 32 instructions, 4 per wave; B: 16, 2 per wave.
-    constexpr int nA = kRbM / 8 / 8, nB = kRbN / 8 / 8, nL = nA + nB;   // per wave
+    // (l % 8) ^ (l / 8).  32 instructions each for A and B, 2 of each per wave.
+    constexpr int nA = kRbM / 8 / 16, nB = kRbN / 8 / 16;
     const uint32_t lane_src = (uint32_t)(16 * ((lane & 7) ^ (lane >> 3)));
     uint32_t va[nA], vb[nB];
+    bool bv[nB];                                          // wave-uniform: the rows are V weights
 #pragma unroll
     for (int u = 0; u < nA; ++u)
         va[u] = (uint32_t)min(row0 + 8 * (wave * nA + u) + (lane >> 3), n - 1) * hidden * 2 + lane_src;
 #pragma unroll
-    for (int u = 0; u < nB; ++u) vb[u] = (uint32_t)(8 * (wave * nB + u) + (lane >> 3)) * hidden * 2 + lane_src;
+    for (int u = 0; u < nB; ++u) {
+        const int c = col0 + 8 * (wave * nB + u);       // 8 rows never straddle K and V (kvd % 128 == 0)
+        bv[u] = c >= kvd;
+        vb[u] = (uint32_t)(c - (bv[u] ? kvd : 0) + (lane >> 3)) * hidden * 2 + lane_src;
+    }
     const uint32_t lds_u = lds_u32(lds);
     auto issue = [&](int kt) {
         const uint32_t st_u = lds_u + (uint32_t)((kt % kRbStages) * kRbStage);
@@ -2073,31 +2081,27 @@ __global__ __launch_bounds__(512, 1) void rebuild_kernel(Geometry g, int layer, 
 #pragma unroll
         for (int u = 0; u < nA; ++u) bdma16<false>(ra, va[u], koff, st_u + 1024 * (wave * nA + u));
 #pragma unroll
-        for (int u = 0; u < nB; ++u) bdma16<false>(rw, vb[u], koff, st_u + kRbStageA + 1024 * (wave * nB + u));
+        for (int u = 0; u < nB; ++u)
+            bdma16<false>(bv[u] ? rv : rk, vb[u], koff, st_u + kRbStageA + 1024 * (wave * nB + u));
     };
 
     // wave (wm, wn) computes rows 64 wm .., columns 64 wn ..
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     floatx4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // a lane's operand rows 64 wm + 16 i + n16 (A) and 64 wn + 16 j + n16 (B):
-    // row % 8 = n16 % 8 for every i, j
-    const int swz = n16 & 7;
+    const int swz = n16 & 7;                            // a lane's operand rows are n16 mod 8
 
     const int n_k = hidden / kRbK;
     issue(0);
-    if (n_k > 1) issue(1);
     for (int kt = 0; kt < n_k; ++kt) {
-        // stage kt has landed once at most stage kt + 1's loads are outstanding
-        if (kt + 1 < n_k) __builtin_amdgcn_s_waitcnt(vmcnt_imm(nL));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_s_barrier();                  // every wave's share; stage kt - 1 is free
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));       // stage kt, the only one in flight
+        __builtin_amdgcn_s_barrier();                   // every wave's share; stage kt - 1 is free
         __builtin_amdgcn_sched_barrier(0);
         lds_fence();
-        if (kt + 2 < n_k) issue(kt + 2);
+        if (kt + 1 < n_k) issue(kt + 1);
         const int so = (kt % kRbStages) * kRbStage;
 #pragma unroll
         for (int kb = 0; kb < kRbK / 32; ++kb) {
@@ -2116,7 +2120,7 @@ __global__ __launch_bounds__(512, 1) void rebuild_kernel(Geometry g, int layer, 
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(kLgkm0);            // this wave's reads of stage kt are done
+        __builtin_amdgcn_s_waitcnt(kLgkm0);             // this wave's reads of stage kt are done
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();               // every wave is done with the operand buffers
@@ -2136,33 +2140,32 @@ __global__ __launch_bounds__(512, 1) void rebuild_kernel(Geometry g, int layer, 
         }
     __syncthreads();
     const int b = st.b0 + bi;
-    if (!is_v) {
-        // 256 tokens x 16 chunks of 16 bytes (128 columns: one or two heads)
-        for (int t = tid; t < kRbM * (kRbN / 8); t += 512) {
-            const int tok = t >> 4, ch = t & 15;
-            if (row0 + tok >= n) continue;
-            const int col = col0 + 8 * ch, kh = col / D, d = col % D;
-            uint16_t* dst = (uint16_t*)g.k_ring + ((pair_index(g, layer, b, kh) * g.pair_slots + row0 + tok) * D + d);
-            *(u32x4*)dst = *(const u32x4*)(lds + tok * kRbOut + 16 * ch);
-        }
-    } else {
-        // 32 groups of 8 slots x 128 dims: 8 consecutive slots of one dim
-        for (int t = tid; t < (kRbM / 8) * kRbN; t += 512) {
-            const int grp = t / kRbN, c = t % kRbN;
-            if (row0 + 8 * grp >= n) continue;
-            const int col = col0 - kvd + c, kh = col / D, d = col % D;
-            u32x4 v;
+    // K columns: 256 tokens x 32 chunks of 16 bytes
+    for (int t = tid; t < kRbM * (kRbN / 8); t += 1024) {
+        const int tok = t >> 5, ch = t & 31;
+        const int col = col0 + 8 * ch;
+        if (col >= kvd || row0 + tok >= n) continue;
+        const int kh = col / D, d = col % D;
+        uint16_t* dst = (uint16_t*)g.k_ring + ((pair_index(g, layer, b, kh) * g.pair_slots + row0 + tok) * D + d);
+        *(u32x4*)dst = *(const u32x4*)(lds + tok * kRbOut + 16 * ch);
+    }
+    // V columns: 32 groups of 8 slots x 256 columns, 8 consecutive slots of one dim
+    for (int t = tid; t < (kRbM / 8) * kRbN; t += 1024) {
+        const int grp = t / kRbN, c = t % kRbN;
+        const int col = col0 + c;
+        if (col < kvd || row0 + 8 * grp >= n) continue;
+        const int kh = (col - kvd) / D, d = (col - kvd) % D;
+        u32x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = *(const uint16_t*)(lds + (8 * grp + 2 * e) * kRbOut + 2 * c);
-                const uint32_t hi = *(const uint16_t*)(lds + (8 * grp + 2 * e + 1) * kRbOut + 2 * c);
-                v[e] = lo | (hi << 16);
-            }
-            const int slot0 = row0 + 8 * grp;
-            uint16_t* dst = (uint16_t*)g.v_ring +
-                            ((pair_index(g, layer, b, kh) * (g.pair_slots / 8) + slot0 / 8) * (int64_t)D + d) * 8;
-            *(u32x4*)dst = v;
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = *(const uint16_t*)(lds + (8 * grp + 2 * e) * kRbOut + 2 * c);
+            const uint32_t hi = *(const uint16_t*)(lds + (8 * grp + 2 * e + 1) * kRbOut + 2 * c);
+            v[e] = lo | (hi << 16);
         }
+        const int slot0 = row0 + 8 * grp;
+        uint16_t* dst = (uint16_t*)g.v_ring +
+                        ((pair_index(g, layer, b, kh) * (g.pair_slots / 8) + slot0 / 8) * (int64_t)D + d) * 8;
+        *(u32x4*)dst = v;
     }
 }
 
@@ -2318,7 +2321,7 @@ hipError_t launch_rebuild(const Geometry& g, int layer, const StreamBatch& st, i
     const int n_col_tiles = 2 * g.hkv * g.d / kRbN;
     const int tiles = st.nb * n_row_tiles;
     const int blocks = 8 * n_col_tiles * ((tiles + 7) / 8);
-    hipLaunchKernelGGL(rebuild_kernel, dim3(blocks), dim3(512), 0, s, g, layer, st, n, hidden, (const uint16_t*)h,
+    hipLaunchKernelGGL(rebuild_kernel, dim3(blocks), dim3(1024), 0, s, g, layer, st, n, hidden, (const uint16_t*)h,
                        (const uint16_t*)wk, (const uint16_t*)wv, n_row_tiles, n_col_tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
