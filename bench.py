@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -252,8 +253,14 @@ def attention_flops(wl, live):
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the kernel source's code, with its
+    comments removed and whitespace collapsed: counters stay tied to the code
+    they were taken on, and an edit to a comment does not void them."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        src = f.read()
+    code = re.sub(r"//[^\n]*|/\*.*?\*/", " ", src, flags=re.S)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_from_profiles(workload):

@@ -1966,9 +1966,10 @@ hipError_t run_decode_mfma(const Geometry& g, int layer, const StreamBatch& st, 
                            int n_cu, const void* k_new, const void* v_new, hipStream_t s) {
     // one resident block per CU (two waves per SIMD); the split count is
     // rounded down to a power of two: each level of the merge tree adds an
-    // exchange latency (about 1.4 us), so a count between two powers pays the
-    // upper one's levels for less walk saved (one 3B stream: 16 splits, one
-    // visit per wave, 11.0 us; 8 splits 11.9; 4 splits 15.2)
+    // exchange round trip (about 0.75 us for one 3B stream, whose four levels
+    // take 3.0 of its 10.7 us), so a count between two powers pays the upper
+    // one's levels for less walk saved (one 3B stream: 16 splits, one visit
+    // per wave, 11.0 us; 8 splits 11.9; 4 splits 15.2)
     int n_split = pick_splits(st.nb * g.hkv, g.w_pad / kTile, n_cu, 4);
     n_split = n_split >= 16 ? 16 : n_split >= 8 ? 8 : n_split >= 4 ? 4 : n_split >= 2 ? 2 : 1;   // the merge tree
                                                                                                // needs a power of two
