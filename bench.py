@@ -363,7 +363,23 @@ def rebuild_timing(args, torch, cache, wl, ring_ms_per_step, gen):
     ms_layer = ms_full / NL
     flops_layer = 2.0 * B * w * hidden * (2 * hkv * d)
     bytes_layer = B * w * hidden * 2 + 2 * hkv * d * hidden * 2 + 2 * B * w * hkv * d * 2
-    del h, wk, wv
+
+    # the same product through the vendor library (torch.mm -> hipBLASLt), as a
+    # linear layer computes it: [B*W x hidden] x [K;V weights]^T into one dense
+    # output (not scattered into a ring); a reference point, not the path
+    h2 = h.view(bf).view(B * w, hidden)
+    wkv = torch.cat([wk, wv]).view(bf)
+    out = torch.empty((B * w, 2 * hkv * d), device="cuda", dtype=bf)
+    for _ in range(3):
+        torch.mm(h2, wkv.t(), out=out)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(NL):
+        torch.mm(h2, wkv.t(), out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    lib_ms = e0.elapsed_time(e1) / NL
+    del h, wk, wv, h2, wkv, out
     return {
         "hidden_dim": hidden,
         "tokens_per_stream": w,
@@ -375,6 +391,7 @@ def rebuild_timing(args, torch, cache, wl, ring_ms_per_step, gen):
         "ring_ms_per_step": round(ring_ms_per_step, 5),
         "full_rebuild_over_ring_step": round(ms_full / ring_ms_per_step, 1),
         "amortized_ms_per_step_rebuilt_every_W_steps": round(ms_full / w, 5),
+        "library_gemm_ms_per_layer": round(lib_ms, 4),
         "note": ("window re-prefill of the K/V projections only: a decoder's re-prefill also recomputes "
                  "the hidden states through every layer below, which this does not count"),
     }
