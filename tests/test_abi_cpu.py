@@ -173,3 +173,63 @@ def test_reset_applies_to_all_layers_and_default_slot():
     for l in range(4):
         assert led.get(l, 1) == (123, 0, 3)
         assert led.get(l, 0) == (7, 7, 7)
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """A C11 program (gcc, -pedantic -Werror) includes the header, takes the
+    address of every declared function, links against the library and runs its
+    host-only calls: the boundary is a C ABI, not a C++ one."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    assert gcc, "gcc not found"
+    names = declared_functions()
+    src = tmp_path / "use_a8r.c"
+    src.write_text("\n".join([
+        "#include <stddef.h>",
+        "#include <stdio.h>",
+        "#include <string.h>",
+        '#include "a8r.h"',
+        '_Static_assert(sizeof(a8r_config) == 64, "a8r_config is 64 bytes");',
+        '_Static_assert(offsetof(a8r_config, rope_theta) == 40, "rope_theta at 40");',
+        "typedef void (*any_fn)(void);",
+        "static const any_fn every_call[] = {",
+        *[f"    (any_fn){n}," for n in names],
+        "};",
+        "int main(void) {",
+        "    a8r_config cfg;",
+        "    memset(&cfg, 0, sizeof cfg);",
+        "    cfg.n_layers = 36; cfg.n_streams = 64; cfg.n_q_heads = 16; cfg.n_kv_heads = 2;",
+        "    cfg.head_dim = 128; cfg.window = 4096; cfg.max_chunk = 8; cfg.dtype = A8R_BF16;",
+        "    cfg.rope_theta = 1.0e6;",
+        "    size_t ws = a8r_workspace_bytes(&cfg);",
+        "    if (ws < (size_t)2 * 36 * 64 * 2 * 4096 * 128 * 2) return 2;",
+        "    cfg.n_layers = 0;",
+        "    a8r_cache* c = NULL;",
+        "    if (a8r_cache_create(&cfg, NULL, NULL, 0, &c) != A8R_EINVAL || c != NULL) return 3;",
+        "    if (strlen(a8r_last_error()) == 0) return 4;",
+        "    a8r_ledger* led = NULL;",
+        "    if (a8r_ledger_create(1, 1, 3, &led) != A8R_OK) return 5;",
+        "    int32_t slots[5]; int64_t ev[5]; int64_t p; int32_t l, s;",
+        "    for (int i = 0; i < 5; ++i)",
+        "        if (a8r_ledger_append(led, 0, 0, 1, 1, &slots[i], &ev[i]) != A8R_OK) return 6;",
+        "    if (a8r_ledger_get(led, 0, 0, &p, &l, &s) != A8R_OK) return 7;",
+        "    a8r_ledger_destroy(led);",
+        "    /* five tokens into a ring of three: slots 0 1 2 0 1, positions 0 and 1 evicted */",
+        "    if (slots[3] != 0 || slots[4] != 1 || ev[2] != -1 || ev[3] != 0 || ev[4] != 1) return 8;",
+        "    if (p != 5 || l != 3 || s != 2) return 9;",
+        '    printf("%s: %zu calls, workspace %zu bytes\\n", a8r_version(),',
+        "           sizeof every_call / sizeof every_call[0], ws);",
+        "    return 0;",
+        "}",
+    ]) + "\n")
+    exe = tmp_path / "use_a8r"
+    libdir = os.path.dirname(a8r.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I",
+                        os.path.join(ROOT, "include"), str(src), "-o", str(exe), f"-L{libdir}", "-l:liba8r.so",
+                        f"-Wl,-rpath,{libdir}", "-Wl,--allow-shlib-undefined"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert f"{len(names)} calls" in r.stdout
