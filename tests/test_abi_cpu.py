@@ -226,7 +226,7 @@ def test_header_is_plain_c_and_links(tmp_path):
     exe = tmp_path / "use_a8r"
     libdir = os.path.dirname(a8r.LIB_PATH)
     r = subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I",
-                        os.path.join(ROOT, "include"), str(src), "-o", str(exe), f"-L{libdir}", "-l:liba8r.so",
+                        os.path.join(ROOT, "include"), str(src), "-o", str(exe), os.path.abspath(a8r.LIB_PATH),
                         f"-Wl,-rpath,{libdir}", "-Wl,--allow-shlib-undefined"],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr

@@ -28,7 +28,7 @@ def test_c_program_closed_forms(tmp_path):
     r = subprocess.run([gcc, "-std=c11", "-O1", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
                         "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"),
                         os.path.join(ROOT, "tests", "c", "closed_form.c"), "-o", str(exe),
-                        f"-L{libdir}", "-l:liba8r.so", f"-L{ROCM}/lib", "-lamdhip64", "-lm",
+                        os.path.abspath(a8r.LIB_PATH), f"-L{ROCM}/lib", "-lamdhip64", "-lm",
                         f"-Wl,-rpath,{libdir}", f"-Wl,-rpath,{ROCM}/lib"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
